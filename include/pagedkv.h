@@ -1,0 +1,154 @@
+/*
+ * pagedkv.h -- C ABI of the paged-KV attention hot path on AMD Instinct MI355X (gfx950).
+ *
+ * One attention layer of a GQA decoder step, as three operations on one GPU:
+ *   kv_store             scatter each new token's K/V row into a paged cache by slot_mapping;
+ *   attn_prefill_varlen  causal attention over sequences packed by cu_seqlens, reading K/V either from
+ *                        this step's rows or, for prefix-cache / chunked prefill, from the paged cache;
+ *   attn_decode_paged    one query per sequence against its whole history in the paged cache;
+ * plus kv_slot_mapping, which builds slot_mapping from the block tables on the device.
+ *
+ * Sources (three web pages on the attention layer of nano-vLLM; cited by tag, title and section):
+ *   [P1] "Nano-VLLM全代码解析笔记(5)-laynorm和attention", m.demingchina.com/news/18656
+ *   [P2] nano-vllm lesson on the Qwen3 attention sub-layer, www.yeyulingfeng.com/a/738130.html
+ *   [P3] "课程 04 · KV 到底写到了哪一格", diomchen.github.io/lessons/0004-attention-slot-mapping.html
+ *
+ * Conventions shared by every entry point
+ *   Memory.   Every pointer is device memory owned by the caller.  The library allocates nothing, keeps
+ *             no pointer after it returns, and writes only the arrays documented as outputs.
+ *   Streams.  Work is enqueued on `stream` (NULL = the default stream) and the call returns without
+ *             waiting.  Issuing kv_store and then an attention call on the same stream gives the
+ *             store-before-attend order the method needs [P3 §4 note].
+ *   Layout.   Token rows are [heads, head_dim] with head_dim contiguous; `*_stride` arguments are the
+ *             distance between consecutive token rows, in elements (>= heads * head_dim), so rows sliced
+ *             out of a merged qkv buffer can be passed as they are.  A paged cache is
+ *             [num_blocks, block_size, num_kv_heads, head_dim], contiguous: slot s = block * block_size +
+ *             cell holds elements [s*D, s*D + D) with D = num_kv_heads * head_dim [P2 §5.1; P3 §2].
+ *   Metadata. int32 arrays, as on the pages [P3 §1 table]: cu_seqlens [batch+1] prefix sums,
+ *             block_tables [batch, max_blocks_per_seq] row-major padded with -1, context_lens [batch].
+ *   Heads.    Query head h reads kv head h / (num_q_heads / num_kv_heads): consecutive groups share a
+ *             kv head [P2 §3].
+ *   Types.    PKV_BF16 (raw bf16 storage, float32 accumulation, outputs rounded to nearest-even) or
+ *             PKV_F32 (float32 throughout).
+ *   Errors.   Arguments are checked on the host before anything is enqueued.  A nonzero return means
+ *             nothing was launched (except PKV_ERR_HIP, reported by the launch itself); pkv_last_error()
+ *             then describes the failure.  No call aborts the process.
+ *   Device-side values (slot_mapping, block tables, cu_seqlens, context_lens) cannot be checked without
+ *   a copy to the host; they are clamped so that no kernel ever reads or writes outside the buffers the
+ *   sizes describe, but out-of-range values give unspecified (not faulting) results, noted per call.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1, /* a null pointer, a negative size, inconsistent shapes or strides */
+  PKV_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement (e.g. head_dim > 256) */
+  PKV_ERR_WORKSPACE = -3,   /* attn_decode_paged: workspace missing or smaller than required */
+  PKV_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+};
+
+/* Thread-local, NUL-terminated description of the last nonzero return on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/*
+ * kv_slot_mapping -- the cache slot of every token this step writes [P3 §2; §9 exercise C].
+ *
+ * Slot of position p of sequence b: block_tables[b][p / block_size] * block_size + p % block_size.
+ * Prefill mode (context_lens == NULL): token rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) are the last
+ *   Lq = cu_seqlens_q[b+1]-cu_seqlens_q[b] of Lk = cu_seqlens_k[b+1]-cu_seqlens_k[b] positions, i.e.
+ *   positions Lk-Lq .. Lk-1 (cu_seqlens_k == NULL means Lk = Lq: nothing cached before this step).
+ * Decode mode (context_lens != NULL, both cu_seqlens NULL): row b is position context_lens[b]-1.
+ * Output slot_mapping [num_tokens]: rows past the last token (cu_seqlens_q[batch], or batch in decode
+ *   mode) are -1, the padding marker kv_store skips [P2 §5.1].  A position below 0, a logical block past
+ *   max_blocks_per_seq, or a negative block-table entry also gives -1.
+ * Requires: block_size >= 1; batch >= 0; num_tokens >= 0; cu_seqlens_q nondecreasing from 0 (device).
+ */
+int kv_slot_mapping(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* context_lens,
+                    const int32_t* block_tables, int32_t batch, int32_t max_blocks_per_seq,
+                    int32_t block_size, int32_t num_tokens, int32_t* slot_mapping, hipStream_t stream);
+
+/*
+ * kv_store -- store_kvcache: copy token row i of key and of value to cache slot slot_mapping[i]
+ * [P2 §5.1 (the three changes from the scatter skeleton); P3 §3; P1 attention.py walkthrough].
+ *
+ * key, value: [num_tokens, num_kv_heads, head_dim], token stride key_stride / value_stride (elements).
+ * k_cache, v_cache: paged caches with num_slots = num_blocks * block_size slots of D elements (in/out).
+ * slot_mapping: [num_tokens].  A slot < 0 (the pages use -1) or >= num_slots is skipped, and bytes of
+ *   slots nobody writes are left as they were.  The copy is bit-exact.  Two tokens with the same slot
+ *   race (the pages never produce that).
+ */
+int kv_store(const void* key, int64_t key_stride, const void* value, int64_t value_stride, void* k_cache,
+             void* v_cache, int64_t num_slots, const int32_t* slot_mapping, int32_t num_tokens,
+             int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype, hipStream_t stream);
+
+/*
+ * attn_prefill_varlen -- varlen attention for a prefill step [P2 §5.3; P3 §4; P1 Q6 §3].
+ *
+ * Sequence b has query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q (token stride q_stride) and
+ * Lk = cu_seqlens_k[b+1]-cu_seqlens_k[b] keys.  Its Lq queries are its last Lq positions: with causal=1
+ * query i sees keys 0 .. Lk-Lq+i (bottom-right alignment; a query with no visible key gets zeros); with
+ * causal=0 it sees all Lk keys.  out[i] = softmax(softmax_scale * q_i K^T) V over the visible keys.
+ *   Contiguous mode (block_tables == NULL): k, v are [num_k_rows, num_kv_heads, head_dim] with token
+ *     strides k_stride / v_stride, and sequence b's keys are rows [cu_seqlens_k[b], cu_seqlens_k[b+1]).
+ *   Paged mode (block_tables != NULL): k, v are the paged caches (num_k_rows = num_blocks * block_size
+ *     slots; k_stride and v_stride are ignored) and key j of sequence b is read from slot
+ *     block_tables[b][j / block_size] * block_size + j % block_size -- the prefix-cache branch, where
+ *     the new tokens were stored first and are read back with the cached prefix [P2 §5.3].
+ * out: [num_q_tokens, num_q_heads, head_dim], contiguous, same dtype as q.
+ * max_seqlen_q must be >= every Lq (rows beyond it are not computed); max_seqlen_k is accepted for
+ *   signature parity with the pages' call and only checked to be >= 0.
+ * Unspecified (but in-bounds) results: query rows past num_q_tokens are skipped; key rows past
+ *   num_k_rows and block-table entries outside [0, num_blocks) are treated as masked.
+ */
+int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                        int64_t v_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t batch, int32_t num_q_tokens,
+                        int64_t num_k_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        float softmax_scale, int32_t causal, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, int32_t block_size, void* out, pkv_dtype dtype,
+                        hipStream_t stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_paged needs for these sizes
+ * (0 if none).  The split of long contexts into independently reduced pieces depends only on these
+ * arguments, so the same workspace serves every call with the same sizes.
+ */
+size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype dtype);
+
+/*
+ * attn_decode_paged -- single-token decode over the paged cache [P2 §5.3 decode call; P3 §4 point 2].
+ *
+ * q: [batch, num_q_heads, head_dim] with token stride q_stride (the pages' [batch, 1, heads, dim] with
+ *   the unit axis dropped).  Sequence b attends over its context_lens[b] cached keys, the newest one
+ *   included (store it first) [P3 §4 note]; key j is at slot block_tables[b][j / block_size] *
+ *   block_size + j % block_size.  context_lens[b] <= 0 gives a zero output row (padding entries).
+ * k_cache, v_cache: [num_blocks, block_size, num_kv_heads, head_dim].
+ * out: [batch, num_q_heads, head_dim], contiguous.
+ * workspace: device memory of at least attn_decode_workspace_bytes(...) bytes (may be NULL when that is
+ *   0); its contents on entry do not matter and are overwritten.
+ * Unspecified (but in-bounds) results: context_lens above max_blocks_per_seq * block_size are clamped to
+ *   it; block-table entries outside [0, num_blocks) are treated as masked keys.
+ */
+int attn_decode_paged(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                      int32_t num_blocks, const int32_t* context_lens, const int32_t* block_tables,
+                      int32_t batch, int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, float softmax_scale, void* out,
+                      void* workspace, size_t workspace_bytes, pkv_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

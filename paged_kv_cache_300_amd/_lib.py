@@ -1,0 +1,230 @@
+"""ctypes binding of the C ABI in include/pagedkv.h (argument marshalling only)."""
+
+import ctypes
+import os
+
+import torch
+
+PKV_F32 = 0
+PKV_BF16 = 1
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG_DIR, "libpagedkv.so")
+_lib = None
+
+_c_i32p = ctypes.c_void_p  # all device pointers travel as void*
+
+
+class PagedKVError(RuntimeError):
+    """A nonzero return from the C ABI; ``code`` is the PKV_ERR_* value."""
+
+    def __init__(self, func, code, message):
+        super().__init__(f"{func} failed with code {code}: {message}")
+        self.code = code
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded ``libpagedkv.so``; raises RuntimeError if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_300_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.pkv_last_error.argtypes = []
+    L.pkv_last_error.restype = ctypes.c_char_p
+    L.kv_slot_mapping.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    L.kv_slot_mapping.restype = ctypes.c_int
+    L.kv_store.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i32, i32, i32, ctypes.c_int, vp]
+    L.kv_store.restype = ctypes.c_int
+    L.attn_prefill_varlen.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
+                                      f32, i32, vp, i32, i32, vp, ctypes.c_int, vp]
+    L.attn_prefill_varlen.restype = ctypes.c_int
+    L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode_paged.argtypes = [vp, i64, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz,
+                                    ctypes.c_int, vp]
+    L.attn_decode_paged.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(func, rc):
+    if rc != 0:
+        raise PagedKVError(func, rc, lib().pkv_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype == torch.float32:
+        return PKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _meta(t, name):
+    """int32 metadata: device tensor, contiguous."""
+    if t is None:
+        return None
+    _dev(t, name)
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows(t, name, heads=None):
+    """[tokens, heads, head_dim] with head_dim contiguous and heads packed; returns the token stride."""
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [tokens, heads, head_dim]")
+    if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} needs stride(-1) == 1 and stride(1) == head_dim")
+    if heads is not None and t.shape[1] != heads:
+        raise ValueError(f"{name} has {t.shape[1]} heads, expected {heads}")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1] * t.shape[2]
+
+
+def _cache(t, name):
+    """[num_blocks, block_size, num_kv_heads, head_dim], contiguous."""
+    _dev(t, name)
+    if t.dim() != 4 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [num_blocks, block_size, num_kv_heads, head_dim] tensor")
+    return t
+
+
+def kv_slot_mapping(block_tables, block_size, num_tokens, cu_seqlens_q=None, cu_seqlens_k=None,
+                    context_lens=None, out=None):
+    """slot_mapping [num_tokens] int32 from block tables (prefill: cu_seqlens; decode: context_lens)."""
+    _meta(block_tables, "block_tables")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k), ("context_lens", context_lens)):
+        _meta(t, name)
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [batch, max_blocks]")
+    batch, max_blocks = block_tables.shape
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int32, device=block_tables.device)
+    _meta(out, "out")
+    rc = lib().kv_slot_mapping(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(context_lens), _ptr(block_tables),
+                               batch, max_blocks, block_size, num_tokens, _ptr(out), _stream(block_tables))
+    _check("kv_slot_mapping", rc)
+    return out
+
+
+def kv_store(key, value, k_cache, v_cache, slot_mapping):
+    """store_kvcache: write row i of key/value to slot slot_mapping[i] of the paged caches (in place)."""
+    _dev(key, "key"); _dev(value, "value")
+    _cache(k_cache, "k_cache"); _cache(v_cache, "v_cache")
+    _meta(slot_mapping, "slot_mapping")
+    n, hkv, hd = key.shape
+    ks = _rows(key, "key")
+    vs = _rows(value, "value", hkv)
+    if value.shape != key.shape or k_cache.shape != v_cache.shape:
+        raise ValueError("key/value and k_cache/v_cache shapes must match")
+    if k_cache.shape[2:] != (hkv, hd):
+        raise ValueError("cache rows must be [num_kv_heads, head_dim] of the key rows")
+    if slot_mapping.numel() != n:
+        raise ValueError("slot_mapping must have one entry per token")
+    if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("key, value and caches must share a dtype")
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    rc = lib().kv_store(_ptr(key), ks, _ptr(value), vs, _ptr(k_cache), _ptr(v_cache), num_slots, _ptr(slot_mapping),
+                        n, hkv, hd, _dtype_code(key), _stream(key))
+    _check("kv_store", rc)
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale,
+                        causal=True, block_table=None, out=None):
+    """Varlen (causal) attention; with ``block_table`` the keys come from the paged caches ``k``, ``v``."""
+    _dev(q, "q")
+    _meta(cu_seqlens_q, "cu_seqlens_q"); _meta(cu_seqlens_k, "cu_seqlens_k"); _meta(block_table, "block_table")
+    nq, hq, hd = q.shape
+    qs = _rows(q, "q")
+    if block_table is None:
+        _dev(k, "k"); _dev(v, "v")
+        ks = _rows(k, "k")
+        vs = _rows(v, "v", k.shape[1])
+        hkv, num_k_rows, bs, max_blocks = k.shape[1], k.shape[0], 1, 0
+        if k.shape[0] != v.shape[0] or k.shape[2] != hd or v.shape[2] != hd:
+            raise ValueError("k and v must be [Nk, Hkv, head_dim] with q's head_dim")
+    else:
+        _cache(k, "k_cache"); _cache(v, "v_cache")
+        if k.shape != v.shape or k.shape[3] != hd:
+            raise ValueError("k/v caches must match each other and q's head_dim")
+        hkv, bs = k.shape[2], k.shape[1]
+        num_k_rows = k.shape[0] * k.shape[1]
+        ks = vs = hkv * hd
+        max_blocks = block_table.shape[1]
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+    batch = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if block_table is not None and block_table.shape[0] != batch:
+        raise ValueError("block_table must have one row per sequence")
+    if out is None:
+        out = torch.empty((nq, hq, hd), dtype=q.dtype, device=q.device)
+    elif out.shape != (nq, hq, hd) or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous [Nq, Hq, head_dim] tensor of q's dtype")
+    rc = lib().attn_prefill_varlen(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                   int(max_seqlen_q), int(max_seqlen_k), batch, nq, num_k_rows, hq, hkv, hd,
+                                   float(softmax_scale), 1 if causal else 0, _ptr(block_table), max_blocks, bs,
+                                   _ptr(out), _dtype_code(q), _stream(q))
+    _check("attn_prefill_varlen", rc)
+    return out
+
+
+def attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                                dtype=torch.bfloat16):
+    code = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
+    return int(lib().attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                                 block_size, code))
+
+
+def attn_decode_paged(q, k_cache, v_cache, cache_seqlens, block_table, softmax_scale, out=None, workspace=None):
+    """Single-token decode over the paged cache; q is [B, Hq, hd] (or [B, 1, Hq, hd]); returns [B, Hq, hd]."""
+    _dev(q, "q")
+    if q.dim() == 4 and q.shape[1] == 1:
+        q = q[:, 0]
+    _cache(k_cache, "k_cache"); _cache(v_cache, "v_cache")
+    _meta(cache_seqlens, "cache_seqlens"); _meta(block_table, "block_table")
+    b, hq, hd = q.shape
+    qs = _rows(q, "q")
+    num_blocks, bs, hkv, hd_c = k_cache.shape
+    if k_cache.shape != v_cache.shape or hd_c != hd:
+        raise ValueError("caches must match each other and q's head_dim")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q and caches must share a dtype")
+    if cache_seqlens.numel() != b or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("cache_seqlens [B] and block_table [B, max_blocks] must match q's batch")
+    max_blocks = block_table.shape[1]
+    need = attn_decode_workspace_bytes(b, hq, hkv, hd, max_blocks, bs, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((b, hq, hd), dtype=q.dtype, device=q.device)
+    elif out.shape != (b, hq, hd) or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous [B, Hq, head_dim] tensor of q's dtype")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_decode_paged(_ptr(q), qs, _ptr(k_cache), _ptr(v_cache), num_blocks, _ptr(cache_seqlens),
+                                 _ptr(block_table), b, max_blocks, bs, hq, hkv, hd, float(softmax_scale), _ptr(out),
+                                 _ptr(workspace), ws_bytes, _dtype_code(q), _stream(q))
+    _check("attn_decode_paged", rc)
+    return out

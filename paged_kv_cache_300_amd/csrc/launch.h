@@ -1,0 +1,50 @@
+// Host-side launchers of the gfx950 kernels; arguments are already validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_slot_mapping(const int32_t* cu_q, const int32_t* cu_k, const int32_t* ctx_lens,
+                               const int32_t* block_tables, int batch, int max_blocks, int block_size,
+                               int num_tokens, int32_t* slot_mapping, hipStream_t stream);
+
+// elem_bytes is 2 (bf16) or 4 (f32); strides in elements.
+hipError_t launch_kv_store(const void* key, int64_t key_stride, const void* value, int64_t value_stride,
+                           void* k_cache, void* v_cache, int64_t num_slots, const int32_t* slot_mapping,
+                           int num_tokens, int row_elems, int elem_bytes, hipStream_t stream);
+
+// Any dtype, head_dim <= 256, any block size; prefill (cu_q != NULL) or decode (ctx_lens != NULL).
+struct AttnArgs {
+  const void* q; int64_t q_stride;
+  const void* k; int64_t k_stride;
+  const void* v; int64_t v_stride;
+  const int32_t* cu_q; const int32_t* cu_k; const int32_t* ctx_lens;
+  const int32_t* block_tables; int max_blocks; int block_size;
+  int64_t num_k_rows;  // contiguous rows, or slots of the paged cache
+  int num_blocks;      // paged mode
+  int batch; int max_seqlen_q; int num_q_tokens;
+  int num_q_heads; int num_kv_heads; int head_dim;
+  float scale; int causal;
+  void* out;
+};
+
+hipError_t launch_attn_generic(const AttnArgs& a, bool bf16, hipStream_t stream);
+
+// bf16, head_dim 128 decode with split-KV.
+struct DecodePlan {
+  int split_tokens;  // keys per work-group (multiple of 128)
+  int max_splits;    // splits per sequence at the longest context
+  size_t workspace_bytes;
+};
+bool decode_fast_supported(int head_dim, int group, bool bf16);
+DecodePlan decode_plan(int batch, int num_q_heads, int num_kv_heads, int max_ctx);
+hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t stream);
+
+// bf16, head_dim 128 prefill on MFMA.
+bool prefill_fast_supported(int head_dim, int group, bool bf16);
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace pkv

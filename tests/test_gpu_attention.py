@@ -1,0 +1,205 @@
+"""GPU parity of attention (prefill contiguous / paged, decode) against the float64 oracle at small sizes that
+still span several tiles, splits and ragged tails; float32 path to 1e-5, bf16 path to 2e-2 (max-abs)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (BF16_TOL, F32_TOL, f64, gpu_slot_mapping, gpu_store_history, host_of, i32, log, max_abs_err,
+                      nan_cache, oracle_attention, oracle_slot_mapping, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_300_amd as m
+    m.lib()
+    return m
+
+
+def _tol(dtype):
+    return BF16_TOL if dtype == "bf16" else F32_TOL
+
+
+def _run_step(pkv, case, paged):
+    """Store history + new tokens through the HIP path, then attention; returns (out, kc, vc, slot_mapping)."""
+    kc, vc = nan_cache(case), nan_cache(case)
+    gpu_store_history(case, kc, vc)
+    sm = gpu_slot_mapping(case)
+    k, v, q = to_dev(case.k, case.dtype), to_dev(case.v, case.dtype), to_dev(case.q, case.dtype)
+    pkv.kv_store(k, v, kc, vc, sm)
+    bt = i32(case.block_tables)
+    if case.decode:
+        out = pkv.attn_decode_paged(q, kc, vc, i32(case.context_lens), bt, case.scale)
+    elif paged:
+        out = pkv.attn_prefill_varlen(q, kc, vc, i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), int(case.Lq.max()),
+                                      int(case.Lk.max()), case.scale, causal=True, block_table=bt)
+    else:
+        out = pkv.attn_prefill_varlen(q, k, v, i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), int(case.Lq.max()),
+                                      int(case.Lk.max()), case.scale, causal=True)
+    torch.cuda.synchronize()
+    return out, kc, vc, sm
+
+
+def _check_attention(case, out, rows=None):
+    want = oracle_attention(case, rows)
+    got = oracle.as_f64(to_host(out), case.dtype)
+    worst = 0.0
+    for b, w in want.items():
+        q0 = int(case.cu_seqlens_q[b])
+        worst = max(worst, max_abs_err(got[q0:q0 + w.shape[0]], w))
+    log(f"  max-abs error {worst:.3e} (tol {_tol(case.dtype):.0e})")
+    assert worst <= _tol(case.dtype)
+    return worst
+
+
+def test_workload1_tiny_fp32_end_to_end(pkv):
+    """Workload 1: store + causal prefill (contiguous and paged), then one decode step per sequence."""
+    pre = workloads.workload1()
+    log(f"workload 1 block_tables={pre.block_tables.tolist()}")
+    for paged in (False, True):
+        out, kc, vc, sm = _run_step(pkv, pre, paged)
+        np.testing.assert_array_equal(to_host(sm), oracle_slot_mapping(pre))
+        _check_attention(pre, out)
+    # cache bytes after the prefill store equal the oracle's store, NaN-poisoned slots included
+    cache = workloads.nan_cache_host(pre.num_blocks, pre.block_size, 2, 16, "f32")
+    want_k, want_v = oracle.store_ref(pre.k, pre.v, cache, cache, oracle_slot_mapping(pre))
+    assert np.array_equal(to_host(kc).view(np.uint32), want_k.view(np.uint32))
+    assert np.array_equal(to_host(vc).view(np.uint32), want_v.view(np.uint32))
+    # decode step on top of the same cache
+    dec = workloads.workload1_decode(pre)
+    sm_d = gpu_slot_mapping(dec)
+    want_sm = oracle_slot_mapping(dec)
+    np.testing.assert_array_equal(to_host(sm_d), want_sm)
+    assert want_sm.tolist() == [int(pre.block_tables[0, 1]) * 4 + 2, int(pre.block_tables[1, 0]) * 4 + 3]
+    pkv.kv_store(to_dev(dec.k, "f32"), to_dev(dec.v, "f32"), kc, vc, sm_d)
+    out = pkv.attn_decode_paged(to_dev(dec.q, "f32"), kc, vc, i32(dec.context_lens), i32(dec.block_tables), dec.scale)
+    torch.cuda.synchronize()
+    _check_attention(dec, out)
+
+
+DECODE_CASES = [
+    # (dtype, hq, hkv, hd, bs, context lengths, seed)
+    ("bf16", 16, 8, 128, 256, [1, 2, 255, 256, 257, 600, 1000, 1300], 11),
+    ("bf16", 16, 8, 128, 16, [5, 100, 1029, 31, 0, 300], 12),
+    ("bf16", 8, 8, 128, 3, [7, 64, 300, 1], 13),
+    ("bf16", 16, 4, 128, 1, [65, 200, 3], 14),
+    ("bf16", 16, 2, 128, 32, [700, 33], 15),  # group of 8: generic path
+    ("bf16", 8, 4, 64, 8, [100, 9, 513], 16),   # head_dim 64: generic path
+    ("f32", 4, 2, 16, 4, [1, 7, 30, 100], 17),
+    ("f32", 16, 8, 128, 256, [300, 1], 18),
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,hd,bs,ctx,seed", DECODE_CASES)
+def test_decode_small(pkv, dtype, hq, hkv, hd, bs, ctx, seed):
+    num_blocks = sum(math.ceil(c / bs) for c in ctx) + 3
+    case = workloads.decode_case(ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, block_size=bs,
+                                 num_blocks=num_blocks, dtype=dtype, seed=seed,
+                                 max_blocks=max(math.ceil(c / bs) for c in ctx) + 1)
+    log(f"decode {dtype} {hq}/{hkv}/{hd} bs={bs} ctx={ctx}")
+    out, kc, vc, sm = _run_step(pkv, case, paged=True)
+    np.testing.assert_array_equal(to_host(sm), oracle_slot_mapping(case))
+    _check_attention(case, out)
+    if 0 in ctx:
+        assert bool((out[ctx.index(0)] == 0).all())
+
+
+PREFILL_CASES = [
+    # (dtype, hq, hkv, hd, bs, new lengths, cached prefix lengths, seed)
+    ("bf16", 16, 8, 128, 256, [1, 63, 64, 65, 200, 333], [0] * 6, 21),
+    ("bf16", 16, 8, 128, 256, [130, 17, 64, 1], [300, 0, 511, 1000], 22),
+    ("bf16", 16, 8, 128, 16, [77, 5], [40, 3], 23),
+    ("bf16", 8, 8, 128, 7, [50, 129], [0, 20], 24),
+    ("bf16", 16, 4, 128, 64, [96, 3], [10, 0], 25),
+    ("bf16", 16, 2, 128, 32, [40], [30], 26),       # group of 8: generic path
+    ("bf16", 4, 2, 32, 4, [33, 8], [5, 0], 27),       # head_dim 32: generic path
+    ("f32", 4, 2, 16, 4, [6, 3, 17], [0, 0, 9], 28),
+    ("f32", 16, 8, 128, 256, [70, 1], [0, 300], 29),
+]
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype,hq,hkv,hd,bs,lq,prefix,seed", PREFILL_CASES)
+def test_prefill_small(pkv, dtype, hq, hkv, hd, bs, lq, prefix, seed, paged):
+    if not paged and any(prefix):
+        pytest.skip("a cached prefix is only readable through the block tables")
+    lk = [a + b for a, b in zip(lq, prefix)]
+    num_blocks = sum(math.ceil(c / bs) for c in lk) + 2
+    case = workloads.make_case(lq, lk, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, block_size=bs,
+                               num_blocks=num_blocks, dtype=dtype, seed=seed)
+    log(f"prefill {dtype} {hq}/{hkv}/{hd} bs={bs} lq={lq} prefix={prefix} paged={paged}")
+    out, kc, vc, sm = _run_step(pkv, case, paged)
+    np.testing.assert_array_equal(to_host(sm), oracle_slot_mapping(case))
+    _check_attention(case, out)
+
+
+def test_prefill_strided_qkv_from_merged_projection(pkv):
+    """q, k, v sliced out of one merged [N, (Hq + 2 Hkv) * hd] buffer, as the pages' split of qkv_proj."""
+    rng = np.random.default_rng(31)
+    lens, hq, hkv, hd = [70, 129], 16, 8, 128
+    n = sum(lens)
+    qkv = workloads.f32_to_bf16_bits(rng.standard_normal((n, (hq + 2 * hkv) * hd)).astype(np.float32))
+    dev = to_dev(qkv, "bf16")
+    q = dev[:, : hq * hd].view(n, hq, hd)
+    k = dev[:, hq * hd: (hq + hkv) * hd].view(n, hkv, hd)
+    v = dev[:, (hq + hkv) * hd:].view(n, hkv, hd)
+    cu = np.array([0, lens[0], n], np.int32)
+    out = pkv.attn_prefill_varlen(q, k, v, i32(cu), i32(cu), max(lens), max(lens), 1 / math.sqrt(hd))
+    torch.cuda.synchronize()
+    qf = oracle.as_f64(qkv[:, : hq * hd].reshape(n, hq, hd), "bf16")
+    kf = oracle.as_f64(qkv[:, hq * hd: (hq + hkv) * hd].reshape(n, hkv, hd), "bf16")
+    vf = oracle.as_f64(qkv[:, (hq + hkv) * hd:].reshape(n, hkv, hd), "bf16")
+    want = oracle.attention_ref(qf, kf, vf, cu, cu, 1 / math.sqrt(hd))
+    err = max_abs_err(oracle.as_f64(to_host(out), "bf16"), want)
+    log(f"  strided max-abs {err:.3e}")
+    assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_non_causal(pkv, dtype):
+    hd = 128 if dtype == "bf16" else 16
+    case = workloads.make_case([40, 90], [40, 90], num_q_heads=16, num_kv_heads=8, head_dim=hd, block_size=256,
+                               num_blocks=4, dtype=dtype, seed=41)
+    q, k, v = (to_dev(x, dtype) for x in (case.q, case.k, case.v))
+    out = pkv.attn_prefill_varlen(q, k, v, i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), 90, 90, case.scale,
+                                  causal=False)
+    torch.cuda.synchronize()
+    want = oracle.attention_ref(f64(case.q, dtype), f64(case.k, dtype), f64(case.v, dtype), case.cu_seqlens_q,
+                                case.cu_seqlens_k, case.scale, causal=False)
+    assert max_abs_err(oracle.as_f64(to_host(out), dtype), want) <= _tol(dtype)
+
+
+def test_single_key_is_exact_in_bf16(pkv):
+    """Closed form: a row that sees one key returns that key's V exactly, even in bf16."""
+    case = workloads.decode_case([1, 1, 1], num_blocks=4, seed=51)
+    out, *_ = _run_step(pkv, case, paged=True)
+    v_new = to_dev(case.v, "bf16")
+    for b in range(3):
+        for h in range(16):
+            assert torch.equal(out[b, h], v_new[b, h // 2])
+    pre = workloads.make_case([1, 1], [1, 1], num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+                              num_blocks=2, dtype="bf16", seed=52)
+    for paged in (False, True):
+        out, *_ = _run_step(pkv, pre, paged)
+        v_new = to_dev(pre.v, "bf16")
+        for h in range(16):
+            assert torch.equal(out[:, h], v_new[:, h // 2])
+
+
+def test_zero_query_gives_prefix_means(pkv):
+    """Closed form: q = 0 makes every visible key equally weighted (causal prefix means of V)."""
+    case = workloads.make_case([150], [150], num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+                               num_blocks=2, dtype="bf16", seed=53)
+    case.q = np.zeros_like(case.q)
+    out, *_ = _run_step(pkv, case, paged=False)
+    v = f64(case.v, "bf16")
+    means = np.cumsum(v, axis=0) / np.arange(1, 151)[:, None, None]
+    got = oracle.as_f64(to_host(out), "bf16")
+    for h in range(16):
+        assert np.max(np.abs(got[:, h] - means[:, h // 2])) <= BF16_TOL

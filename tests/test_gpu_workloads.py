@@ -1,0 +1,154 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the benchmark times.
+
+Inputs are generated on the device from the workload seed; the oracle receives host copies of those inputs
+(never of a kernel's output).  slot_mapping is compared in full (bit-exact), the store on every written row
+plus the poison pattern of every other row, and attention on the sequences listed per test (all of them
+where the oracle finishes in seconds, a seeded sample where it would not)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (BF16_TOL, gpu_slot_mapping, gpu_store_history, host_of, i32, log, max_abs_err, nan_cache,
+                      oracle_attention, oracle_slot_mapping, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+NAN16 = np.int16(workloads.NAN_BITS["bf16"])
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_300_amd as m
+    m.lib()
+    return m
+
+
+def _poison_rows(cache):
+    """Number of cache slots whose every element still holds the poison pattern."""
+    d = cache.shape[2] * cache.shape[3]
+    bits = cache.view(torch.int16).view(-1, d)
+    return int((bits == int(NAN16)).all(dim=1).sum())
+
+
+def _step(pkv, case, paged, workspace=None):
+    kc, vc = nan_cache(case), nan_cache(case)
+    gpu_store_history(case, kc, vc)
+    sm = gpu_slot_mapping(case)
+    k, v, q = to_dev(case.k, case.dtype), to_dev(case.v, case.dtype), to_dev(case.q, case.dtype)
+    pkv.kv_store(k, v, kc, vc, sm)
+    bt = i32(case.block_tables)
+    if case.decode:
+        out = pkv.attn_decode_paged(q, kc, vc, i32(case.context_lens), bt, case.scale, workspace=workspace)
+    elif paged:
+        out = pkv.attn_prefill_varlen(q, kc, vc, i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), int(case.Lq.max()),
+                                      int(case.Lk.max()), case.scale, causal=True, block_table=bt)
+    else:
+        out = pkv.attn_prefill_varlen(q, k, v, i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), int(case.Lq.max()),
+                                      int(case.Lk.max()), case.scale, causal=True)
+    torch.cuda.synchronize()
+    return out, kc, vc, sm
+
+
+def _check_store(case, kc, vc, sm_host):
+    """Every new token's row sits at its slot, bit for bit; every slot nobody wrote still holds the poison."""
+    d = case.num_kv_heads * case.head_dim
+    rows = np.where(sm_host >= 0)[0]
+    idx = torch.from_numpy(sm_host[rows].astype(np.int64)).cuda()
+    k_new, v_new = to_dev(case.k, case.dtype), to_dev(case.v, case.dtype)
+    r = torch.from_numpy(rows).cuda()
+    assert torch.equal(kc.view(-1, d)[idx].view(torch.int16), k_new.reshape(-1, d)[r].view(torch.int16))
+    assert torch.equal(vc.view(-1, d)[idx].view(torch.int16), v_new.reshape(-1, d)[r].view(torch.int16))
+    written = int(case.cu_hist[-1]) + len(rows)
+    untouched = case.num_blocks * case.block_size - written
+    assert _poison_rows(kc) == untouched and _poison_rows(vc) == untouched
+
+
+def _check_attention(case, out, seqs):
+    want = oracle_attention(case, seqs)
+    got = oracle.as_f64(to_host(out), case.dtype)
+    worst = 0.0
+    for b, w in want.items():
+        q0 = int(case.cu_seqlens_q[b])
+        worst = max(worst, max_abs_err(got[q0:q0 + w.shape[0]], w))
+    log(f"  attention max-abs error {worst:.3e} over {len(want)} sequences")
+    assert worst <= BF16_TOL
+
+
+def test_workload2_decode_full(pkv):
+    case = workloads.workload2(device="cuda")
+    log(f"workload 2: batch {case.batch}, sum ctx {int(case.Lk.sum())}")
+    out, kc, vc, sm = _step(pkv, case, paged=True)
+    sm_h = to_host(sm)
+    np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
+    _check_store(case, kc, vc, sm_h)
+    _check_attention(case, out, range(case.batch))
+
+
+def test_workload3_varlen_prefill_full(pkv):
+    case = workloads.workload3(device="cuda")
+    log(f"workload 3: lengths {case.Lq.tolist()}")
+    out, kc, vc, sm = _step(pkv, case, paged=False)
+    sm_h = to_host(sm)
+    np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
+    _check_store(case, kc, vc, sm_h)
+    _check_attention(case, out, range(case.batch))
+
+
+def test_workload4_prefix_prefill_full(pkv):
+    case = workloads.workload4(device="cuda")
+    log(f"workload 4: new {case.Lq.tolist()} total {case.Lk.tolist()}")
+    out, kc, vc, sm = _step(pkv, case, paged=True)
+    sm_h = to_host(sm)
+    np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
+    _check_store(case, kc, vc, sm_h)
+    _check_attention(case, out, range(case.batch))
+
+
+def test_workload5_padded_long_decode(pkv):
+    case = workloads.workload5_decode(device="cuda")
+    real = np.where(case.Lk > 0)[0]
+    log(f"workload 5 decode: {len(real)} real rows, sum ctx {int(case.Lk.sum())}")
+    out, kc, vc, sm = _step(pkv, case, paged=True)
+    sm_h = to_host(sm)
+    np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
+    assert np.all(sm_h[224:] == -1)
+    _check_store(case, kc, vc, sm_h)
+    # the oracle on a seeded sample of real rows, always including the shortest and longest context
+    rng = np.random.default_rng(55)
+    sample = sorted(set(rng.choice(real, 10, replace=False).tolist()) |
+                    {int(real[np.argmin(case.Lk[real])]), int(real[np.argmax(case.Lk[real])])})
+    _check_attention(case, out, sample)
+    assert bool((out[224:] == 0).all())  # padding rows
+
+
+def test_workload5_store_sweep_bit_exact(pkv):
+    sweep = workloads.store_sweep(device="cuda")
+    shape = (sweep.num_blocks, sweep.block_size, sweep.num_kv_heads, sweep.head_dim)
+    d = sweep.num_kv_heads * sweep.head_dim
+    for s in range(len(sweep.slots)):
+        kc = torch.full(shape, int(NAN16), dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        vc = kc.clone()
+        slots = sweep.slots[s]
+        pkv.kv_store(sweep.key[s], sweep.value[s], kc, vc, i32(slots))
+        torch.cuda.synchronize()
+        idx = torch.from_numpy(slots.astype(np.int64)).cuda()
+        assert torch.equal(kc.view(-1, d)[idx].view(torch.int16), sweep.key[s].reshape(-1, d).view(torch.int16))
+        assert torch.equal(vc.view(-1, d)[idx].view(torch.int16), sweep.value[s].reshape(-1, d).view(torch.int16))
+        untouched = sweep.num_blocks * sweep.block_size - len(slots)
+        assert _poison_rows(kc) == untouched and _poison_rows(vc) == untouched
+        # the oracle's store on a sample of tokens, row by row
+        rng = np.random.default_rng(s)
+        pick = rng.choice(len(slots), 64, replace=False)
+        key_h = host_of(sweep.key[s][torch.from_numpy(pick).cuda()], "bf16")
+        val_h = host_of(sweep.value[s][torch.from_numpy(pick).cuda()], "bf16")
+        local = np.arange(64, dtype=np.int32)
+        empty = np.full((1, 64, sweep.num_kv_heads, sweep.head_dim), workloads.NAN_BITS["bf16"], np.uint16)
+        want_k, want_v = oracle.store_ref(key_h, val_h, empty, empty, local)
+        got_k = to_host(kc.view(-1, d)[torch.from_numpy(slots[pick].astype(np.int64)).cuda()])
+        got_v = to_host(vc.view(-1, d)[torch.from_numpy(slots[pick].astype(np.int64)).cuda()])
+        assert np.array_equal(got_k, want_k.reshape(64, d)) and np.array_equal(got_v, want_v.reshape(64, d))
+        del kc, vc
+        torch.cuda.empty_cache()
