@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+Headline: one decode layer-step of workload 2 (batch 64, context_lens U[512,4096], block_size 256, bf16,
+16 q / 8 kv heads, head_dim 128): kv_slot_mapping -> kv_store of the new token -> attn_decode_paged.
+``value`` is the KV-cache bytes the decode must read (sum(context_lens) * 2 * Hkv * hd * 2 B) divided by the
+whole step's time.  Steps rotate over ``--layers`` independent caches (different layers of the model), so
+the 256 MB Infinity Cache cannot hold the working set between steps.
+
+The same JSON line carries:
+  roofline      the decode attention call (split + combine kernels) timed with HIP events on the stream it
+                runs on, against MI355X's 8 TB/s HBM peak; ``traffic`` from rocprofv3 counters kept in
+                profiles/ (null if the kernel source changed since they were taken);
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload, BLAS pinned to one thread;
+  secondary     varlen prefill TFLOP/s (workload 3), prefix-cache prefill TFLOP/s (workload 4), the store
+                sweep GB/s (workload 5, N=16384) and the long padded decode GB/s (workload 5, batch 256).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+PROFILES = os.path.join(ROOT, "profiles")
+METRIC = "paged decode attn KV GB/s (% HBM peak); varlen prefill TFLOP/s; store GB/s"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_300_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, src_hash):
+    """Bytes per launch from committed rocprofv3 counter runs, if they were taken on the current source."""
+    path = os.path.join(PROFILES, f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------------------ GPU side
+
+class Timer:
+    """HIP events on the current stream around one call per step."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        self.i = 0
+
+    def __enter__(self):
+        self.pairs[self.i][0].record()
+        return self
+
+    def __exit__(self, *exc):
+        self.pairs[self.i][1].record()
+        self.i += 1
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs[: self.i]) / max(self.i, 1)
+
+
+def run_steps(torch, step, steps, warmup):
+    """W untimed steps, then exactly K timed steps between device synchronisations."""
+    for i in range(warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    timer = Timer(torch, steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, timer)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return wall_ms, timer.mean_ms()
+
+
+def dev_case_layers(make, layers, torch):
+    """``layers`` independent draws of one workload's tensors (same metadata, different data and caches)."""
+    import workloads
+    out = []
+    for layer in range(layers):
+        case = make(device="cuda")
+        if layer:
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(1000 + layer)
+            for name in ("q", "k", "v", "hist_k", "hist_v"):
+                t = getattr(case, name)
+                setattr(case, name, torch.randn(t.shape, generator=gen, device="cuda").to(t.dtype))
+        out.append(case)
+    return out, workloads
+
+
+def build_caches(pkv, torch, case):
+    import workloads
+    shape = (case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim)
+    kc = torch.full(shape, workloads.NAN_BITS["bf16"], dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vc = kc.clone()
+    n_hist = int(case.cu_hist[-1])
+    if n_hist:
+        hist = torch.from_numpy(case.cu_hist).cuda()
+        bt = torch.from_numpy(case.block_tables).cuda()
+        sm = pkv.kv_slot_mapping(bt, case.block_size, n_hist, cu_seqlens_q=hist, cu_seqlens_k=hist)
+        pkv.kv_store(case.hist_k, case.hist_v, kc, vc, sm)
+        case.hist_k = case.hist_v = None  # the history now lives in the cache only
+    return kc, vc
+
+
+def bench_decode(pkv, torch, make, steps, warmup, layers):
+    cases, _ = dev_case_layers(make, layers, torch)
+    c0 = cases[0]
+    meta = {
+        "bt": torch.from_numpy(c0.block_tables).cuda(),
+        "ctx": torch.from_numpy(c0.context_lens).cuda(),
+    }
+    caches = [build_caches(pkv, torch, c) for c in cases]
+    ws_bytes = pkv.attn_decode_workspace_bytes(c0.batch, c0.num_q_heads, c0.num_kv_heads, c0.head_dim,
+                                               c0.max_blocks, c0.block_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    sm = torch.empty(c0.batch, dtype=torch.int32, device="cuda")
+    outs = [torch.empty_like(c.q) for c in cases]
+    torch.cuda.synchronize()
+
+    def step(i, timer):
+        L = i % layers
+        c, (kc, vc) = cases[L], caches[L]
+        pkv.kv_slot_mapping(meta["bt"], c0.block_size, c0.batch, context_lens=meta["ctx"], out=sm)
+        pkv.kv_store(c.k, c.v, kc, vc, sm)
+        if timer is None:
+            pkv.attn_decode_paged(c.q, kc, vc, meta["ctx"], meta["bt"], c0.scale, out=outs[L], workspace=ws)
+        else:
+            with timer:
+                pkv.attn_decode_paged(c.q, kc, vc, meta["ctx"], meta["bt"], c0.scale, out=outs[L], workspace=ws)
+
+    wall_ms, kern_ms = run_steps(torch, step, steps, warmup)
+    kv_bytes = int(c0.Lk.astype(int).sum()) * 2 * c0.num_kv_heads * c0.head_dim * 2
+    del caches, cases
+    torch.cuda.empty_cache()
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "kv_bytes": kv_bytes, "batch": c0.batch,
+            "sum_ctx": int(c0.Lk.astype(int).sum())}
+
+
+def prefill_flops(case):
+    lq = case.Lq.astype(int)
+    lk = case.Lk.astype(int)
+    pairs = int(sum(q * (k - q) + q * (q + 1) // 2 for q, k in zip(lq, lk)))
+    return 4 * case.head_dim * case.num_q_heads * pairs
+
+
+def bench_prefill(pkv, torch, make, steps, warmup, layers, paged):
+    cases, _ = dev_case_layers(make, layers, torch)
+    c0 = cases[0]
+    bt = torch.from_numpy(c0.block_tables).cuda()
+    cu_q = torch.from_numpy(c0.cu_seqlens_q).cuda()
+    cu_k = torch.from_numpy(c0.cu_seqlens_k).cuda()
+    caches = [build_caches(pkv, torch, c) for c in cases]
+    n = int(c0.cu_seqlens_q[-1])
+    sm = torch.empty(n, dtype=torch.int32, device="cuda")
+    outs = [torch.empty_like(c.q) for c in cases]
+    mq, mk = int(c0.Lq.max()), int(c0.Lk.max())
+    torch.cuda.synchronize()
+
+    def attn(c, kc, vc, L):
+        if paged:
+            pkv.attn_prefill_varlen(c.q, kc, vc, cu_q, cu_k, mq, mk, c0.scale, block_table=bt, out=outs[L])
+        else:
+            pkv.attn_prefill_varlen(c.q, c.k, c.v, cu_q, cu_k, mq, mk, c0.scale, out=outs[L])
+
+    def step(i, timer):
+        L = i % layers
+        c, (kc, vc) = cases[L], caches[L]
+        pkv.kv_slot_mapping(bt, c0.block_size, n, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, out=sm)
+        pkv.kv_store(c.k, c.v, kc, vc, sm)
+        if timer is None:
+            attn(c, kc, vc, L)
+        else:
+            with timer:
+                attn(c, kc, vc, L)
+
+    wall_ms, kern_ms = run_steps(torch, step, steps, warmup)
+    flops = prefill_flops(c0)
+    del caches, cases
+    torch.cuda.empty_cache()
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "flops": flops, "tokens": n}
+
+
+def bench_store(pkv, torch, steps, warmup):
+    import workloads
+    sw = workloads.store_sweep(device="cuda")
+    shape = (sw.num_blocks, sw.block_size, sw.num_kv_heads, sw.head_dim)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    slots = [torch.from_numpy(s).cuda() for s in sw.slots]
+    torch.cuda.synchronize()
+
+    def step(i, timer):
+        s = i % len(slots)
+        if timer is None:
+            pkv.kv_store(sw.key[s], sw.value[s], kc, vc, slots[s])
+        else:
+            with timer:
+                pkv.kv_store(sw.key[s], sw.value[s], kc, vc, slots[s])
+
+    wall_ms, kern_ms = run_steps(torch, step, steps, warmup)
+    n = len(sw.slots[0])
+    row = sw.num_kv_heads * sw.head_dim * 2
+    moved = 2 * n * row * 2 + 4 * n  # read + write of K and V rows, plus the slots
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n}
+
+
+# ------------------------------------------------------------------------------------------------ CPU side
+
+def cpu_baseline(min_seconds=10.0, n_seqs=16):
+    """The oracle's decode step (slot_mapping, store, attention) on the first ``n_seqs`` sequences of
+    workload 2 (same context lengths, shapes and distributions), repeated until ``min_seconds`` elapsed."""
+    import numpy as np
+    import oracle
+    import workloads
+    rng = np.random.default_rng(2)
+    ctx = rng.integers(512, 4096, size=64, endpoint=True)[:n_seqs]
+    case = workloads.decode_case(ctx, num_blocks=sum(math.ceil(int(c) / 256) for c in ctx), seed=2)
+    cache = workloads.nan_cache_host(case.num_blocks, 256, 8, 128, "bf16")
+    hist_sm = oracle.slot_mapping_ref(case.block_tables, 256, int(case.cu_hist[-1]), cu_seqlens_q=case.cu_hist,
+                                      cu_seqlens_k=case.cu_hist)
+    kc, vc = oracle.store_ref(case.hist_k, case.hist_v, cache, cache, hist_sm)
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        reps, secs = _time_oracle_step(case, kc, vc, min_seconds)
+    kv_bytes = int(ctx.sum()) * 2 * 8 * 128 * 2
+    return {"value": round(kv_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"workload 2's first {n_seqs} sequences (sum ctx {int(ctx.sum())}), full decode step "
+                      f"(slot_mapping + store + attention, float64), {reps} repetitions, {secs:.2f} s each"}
+
+
+def _time_oracle_step(case, kc, vc, min_seconds):
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        sm = oracle.slot_mapping_ref(case.block_tables, 256, case.batch, context_lens=case.context_lens)
+        kc2, vc2 = oracle.store_ref(case.k, case.v, kc, vc, sm)
+        oracle.decode_ref(oracle.as_f64(case.q, "bf16"), oracle.as_f64(kc2, "bf16"), oracle.as_f64(vc2, "bf16"),
+                          case.context_lens, case.block_tables, 256, case.scale)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds or reps >= 50:
+            break
+    return reps, (time.perf_counter() - t0) / reps
+
+
+# ------------------------------------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
+    ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_300_amd as pkv
+    import workloads
+    pkv.lib()
+    torch.cuda.set_device(0)
+
+    log("decode, workload 2")
+    dec = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers)
+    achieved = dec["kv_bytes"] / (dec["kernel_ms"] * 1e-3) / 1e9
+    value = dec["kv_bytes"] / (dec["wall_ms"] * 1e-3) / 1e9
+    dec_hash = source_hash("attn_decode.hip", "common.h")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("attn_decode_workload2", dec_hash),
+                "kernel": "attn_decode_paged (split + combine kernels)", "kernel_ms": round(dec["kernel_ms"], 5),
+                "algorithmic_bytes": dec["kv_bytes"], "source_hash": dec_hash}
+
+    secondary = {}
+    if not args.headline_only:
+        log("prefill, workload 3")
+        p3 = bench_prefill(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers, paged=False)
+        log("prefix prefill, workload 4")
+        p4 = bench_prefill(pkv, torch, workloads.workload4, args.steps, args.warmup, args.layers, paged=True)
+        log("store sweep, workload 5")
+        st = bench_store(pkv, torch, args.steps, args.warmup)
+        log("long padded decode, workload 5")
+        d5 = bench_decode(pkv, torch, workloads.workload5_decode, max(args.steps // 5, 3), 2, 2)
+        for name, r in (("varlen_prefill_workload3", p3), ("prefix_prefill_workload4", p4)):
+            tf = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+            secondary[name] = {"value": round(tf, 2), "unit": "TFLOP/s", "frac_bf16_mfma_peak":
+                               round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "kernel_ms": round(r["kernel_ms"], 4),
+                               "step_ms": round(r["wall_ms"], 4), "flops": r["flops"], "tokens": r["tokens"]}
+        gbs = st["bytes"] / (st["kernel_ms"] * 1e-3) / 1e9
+        secondary["store_sweep_workload5"] = {"value": round(gbs, 1), "unit": "GB/s",
+                                             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                             "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
+                                             "tokens": st["tokens"]}
+        gbs5 = d5["kv_bytes"] / (d5["kernel_ms"] * 1e-3) / 1e9
+        secondary["long_decode_workload5"] = {"value": round(gbs5, 1), "unit": "GB/s",
+                                             "frac_hbm_peak": round(gbs5 / HBM_PEAK_GBS, 4),
+                                             "kernel_ms": round(d5["kernel_ms"], 4), "kv_bytes": d5["kv_bytes"],
+                                             "step_ms": round(d5["wall_ms"], 4)}
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu oracle baseline")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workloads.WORKLOADS[2], "batch": dec["batch"], "sum_context_lens": dec["sum_ctx"],
+                   "heads": "16 q / 8 kv", "head_dim": 128, "block_size": 256, "layers_rotated": args.layers,
+                   "step": "kv_slot_mapping + kv_store + attn_decode_paged"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
