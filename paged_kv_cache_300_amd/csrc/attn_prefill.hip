@@ -1,11 +1,315 @@
-// Varlen causal prefill attention, bf16 storage, head_dim 128, on gfx950 MFMA.
+// Varlen causal prefill attention on gfx950 bf16 MFMA (head_dim 128), contiguous or paged K/V.
+//
+// What it computes [P2 §5.3; P3 §4; P1 Q6 §3]: for sequence b, query head h and query row i (the i-th of
+// the sequence's Lq new tokens, at absolute position Lk - Lq + i), o = softmax(scale * q K^T) V over keys
+// 0 .. Lk - Lq + i (causal) or 0 .. Lk - 1; keys come from this step's k/v rows (contiguous mode) or from the
+// paged cache through the block table (prefix-cache / chunked prefill).  Query head h reads kv head
+// h / G, G = Hq / Hkv [P2 §3].
+//
+// How (the FlashAttention tiling of [P2 §5.2], laid out for CDNA4):
+//  * A work-group owns 64 query tokens of one sequence for one kv head and ALL G query heads that share it,
+//    so every K/V tile is loaded once for the whole GQA group.  Its 4 waves own 16 tokens each; a wave's
+//    G heads are G MFMA column blocks over the same 16 tokens (one causal mask serves all of them).
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: Q^T stays in registers as
+//    the B operand for the whole key loop, K rows are read from LDS as the A operand.  In that layout a
+//    lane's accumulators already are the B operand P^T of the second product O^T = V^T P^T, so the
+//    probabilities never leave registers; the per-query softmax statistics sit in the same lane as the
+//    query's output column, so the online rescale [P2 §5.2 ②] is a per-lane multiply.
+//  * K/V tiles of 64 keys are staged through LDS with 16-byte loads, double-buffered: the next tile's global
+//    loads are in flight while the current tile is multiplied; rows are padded (272 B) so the 16 lanes of a
+//    quarter-wave hit distinct banks.
+//  * Softmax in base 2 with log2(e) folded into the scale; the running maximum is shared by the 4 lane
+//    groups of a query (two lane swaps per tile); the normaliser is summed once at the end.
+//  * Only tiles that cross the causal diagonal or the end of the keys are masked.  Work-groups are
+//    launched heaviest query tile first so the long causal rows do not form the tail.
+#include <math.h>
+
 #include "common.h"
 #include "launch.h"
 
 namespace pkv {
+namespace {
 
-bool prefill_fast_supported(int, int, bool) { return false; }
+constexpr int HD = 128;
+constexpr int BM = 64;        // query tokens per work-group
+constexpr int BN = 64;        // keys per tile
+constexpr int THREADS = 256;  // 4 waves x 16 tokens
+constexpr int LROW = HD + 8;  // LDS row pitch in elements (272 bytes)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMinusBig = -1e30f;
 
-hipError_t launch_prefill_bf16(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct PrefillKernelArgs {
+  const uint16_t* q;
+  int64_t q_stride;
+  const uint16_t* k;
+  int64_t k_stride;
+  const uint16_t* v;
+  int64_t v_stride;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* bt;  // null: contiguous mode
+  int max_blocks;
+  int bs;
+  int bs_shift;  // log2(block_size) if a power of two, else -1
+  int num_blocks;
+  int64_t num_k_rows;
+  int num_q_tokens;
+  int num_q_heads;
+  int num_kv_heads;
+  float scale_log2;
+  int causal;
+  int max_tiles;
+  uint16_t* out;
+};
+
+template <int G>
+__global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tile = p.max_tiles - 1 - int(blockIdx.z);  // heaviest (latest) query tiles are dispatched first
+  const int q_start = p.cu_q[b];
+  const int Lq = p.cu_q[b + 1] - q_start;
+  if (tile * BM >= Lq) return;
+  const int64_t k_start = p.cu_k[b];
+  int Lk = max(p.cu_k[b + 1] - p.cu_k[b], 0);
+  if (p.bt) Lk = min(Lk, p.max_blocks * p.bs);
+  const int t0 = tile * BM;
+  const int qpos0 = Lk - Lq + t0;  // absolute position of the work-group's first query row
+  int kend = p.causal ? min(Lk, qpos0 + BM) : Lk;
+  kend = max(kend, 0);
+  const int n_tiles = (kend + BN - 1) / BN;
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * LROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int tok = t0 + wave * 16 + col;  // this lane's query token (column of every MFMA block)
+  const int qpos = Lk - Lq + tok;
+
+  // Q^T operands: head n of the group, dims 32*ks + 8*grp .. +8.
+  uint4 qreg[G][4];
+  {
+    const bool ok = tok < Lq && q_start + tok < p.num_q_tokens;
+    const uint16_t* qrow = p.q + int64_t(q_start + tok) * p.q_stride + int64_t(kvh) * G * HD + grp * 8;
+#pragma unroll
+    for (int n = 0; n < G; ++n)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qreg[n][ks] = ok ? *reinterpret_cast<const uint4*>(qrow + n * HD + ks * 32) : make_uint4(0, 0, 0, 0);
+  }
+
+  // Staging: thread t moves 16-byte chunks c = t + 256 i (i < 4) of the K and V tiles: key c / 16, chunk c % 16.
+  uint4 kst[4], vst[4];
+  const int64_t slot_elems = int64_t(p.num_kv_heads) * HD;
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + THREADS * i;
+      const int key = kt * BN + (c >> 4);
+      const int ch = c & 15;
+      int64_t koff = -1, voff = -1;
+      if (key < Lk) {
+        if (p.bt) {
+          int lb, cell;
+          if (p.bs_shift >= 0) { lb = key >> p.bs_shift; cell = key & (p.bs - 1); }
+          else { lb = key / p.bs; cell = key - lb * p.bs; }
+          const int blk = p.bt[int64_t(b) * p.max_blocks + lb];
+          if (blk >= 0 && blk < p.num_blocks) koff = voff = (int64_t(blk) * p.bs + cell) * slot_elems;
+        } else if (k_start + key >= 0 && k_start + key < p.num_k_rows) {
+          koff = (k_start + key) * p.k_stride;
+          voff = (k_start + key) * p.v_stride;
+        }
+      }
+      const int64_t e = int64_t(kvh) * HD + ch * 8;
+      kst[i] = koff >= 0 ? *reinterpret_cast<const uint4*>(p.k + koff + e) : make_uint4(0, 0, 0, 0);
+      vst[i] = voff >= 0 ? *reinterpret_cast<const uint4*>(p.v + voff + e) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + THREADS * i;
+      const int off = (c >> 4) * LROW + (c & 15) * 8;
+      *reinterpret_cast<uint4*>(&lds_k[buf][off]) = kst[i];
+      *reinterpret_cast<uint4*>(&lds_v[buf][off]) = vst[i];
+    }
+  };
+
+  f32x4_t o[8][G];
+  float m[G], l[G];
+#pragma unroll
+  for (int n = 0; n < G; ++n) {
+    m[n] = kMinusBig;
+    l[n] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_tiles) load_tile(kt + 1);
+
+    // S^T = K Q^T for 4 blocks of 16 keys.
+    f32x4_t s[4][G];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int n = 0; n < G; ++n) s[kb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&lds_k[buf][(kb * 16 + col) * LROW + ks * 32 + grp * 8]);
+#pragma unroll
+        for (int n = 0; n < G; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
+      }
+    }
+
+    // Scale, mask, online softmax.  Lane holds keys kt*64 + 16 kb + 4 grp + r of query `tok`.
+    const bool need_mask = (kt + 1) * BN > Lk || (p.causal && (kt + 1) * BN - 1 > qpos0);
+    uint4 pb[G][2];
+#pragma unroll
+    for (int n = 0; n < G; ++n) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = s[kb][n][r] * p.scale_log2;
+          if (need_mask) {
+            const int kp = kt * BN + kb * 16 + grp * 4 + r;
+            const bool vis = kp < Lk && (!p.causal || kp <= qpos);
+            x = vis ? x : -INFINITY;
+          }
+          s[kb][n][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+      const float mn = fmaxf(m[n], mx);
+      const float alpha = fast_exp2(m[n] - mn);
+      m[n] = mn;
+      float sum = 0.f;
+      float pv[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[kb][r] = fast_exp2(s[kb][n][r] - mn);
+          sum += pv[kb][r];
+        }
+      l[n] = l[n] * alpha + sum;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[d][n] *= alpha;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pb[n][h].x = pack_bf16x2(pv[2 * h][0], pv[2 * h][1]);
+        pb[n][h].y = pack_bf16x2(pv[2 * h][2], pv[2 * h][3]);
+        pb[n][h].z = pack_bf16x2(pv[2 * h + 1][0], pv[2 * h + 1][1]);
+        pb[n][h].w = pack_bf16x2(pv[2 * h + 1][2], pv[2 * h + 1][3]);
+      }
+    }
+
+    // O^T += V^T P^T: A operand = V^T rows (dims), k slots = keys {4 grp + r} and {16 + 4 grp + r} of each
+    // 32-key half, matching the P^T slots filled above.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint16_t* vb = &lds_v[buf][(h * 32 + grp * 4) * LROW];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const int dim = d * 16 + col;
+        uint4 a;
+        a.x = uint32_t(vb[0 * LROW + dim]) | (uint32_t(vb[1 * LROW + dim]) << 16);
+        a.y = uint32_t(vb[2 * LROW + dim]) | (uint32_t(vb[3 * LROW + dim]) << 16);
+        a.z = uint32_t(vb[16 * LROW + dim]) | (uint32_t(vb[17 * LROW + dim]) << 16);
+        a.w = uint32_t(vb[18 * LROW + dim]) | (uint32_t(vb[19 * LROW + dim]) << 16);
+#pragma unroll
+        for (int n = 0; n < G; ++n) o[d][n] = mfma_16x16x32(a, pb[n][h], o[d][n]);
+      }
+    }
+
+    if (kt + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Normalise and write: lane holds dims 16 d + 4 grp + r of query `tok`, head kvh*G + n.
+  float inv[G];
+#pragma unroll
+  for (int n = 0; n < G; ++n) {
+    float lt = l[n];
+    lt += shfl_xor_f32(lt, 16);
+    lt += shfl_xor_f32(lt, 32);
+    inv[n] = lt > 0.f ? 1.f / lt : 0.f;
+  }
+  if (tok < Lq && q_start + tok < p.num_q_tokens) {
+#pragma unroll
+    for (int n = 0; n < G; ++n) {
+      uint16_t* orow = p.out + (int64_t(q_start + tok) * p.num_q_heads + kvh * G + n) * HD + grp * 4;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint2 w;
+        w.x = pack_bf16x2(o[d][n][0] * inv[n], o[d][n][1] * inv[n]);
+        w.y = pack_bf16x2(o[d][n][2] * inv[n], o[d][n][3] * inv[n]);
+        *reinterpret_cast<uint2*>(orow + d * 16) = w;
+      }
+    }
+  }
+}
+
+template <int G>
+hipError_t launch_g(const PrefillKernelArgs& p, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_kernel<G>, dim3(p.num_kv_heads, batch, p.max_tiles), dim3(THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_fast_supported(int head_dim, int group, bool bf16) {
+  return bf16 && head_dim == HD && (group == 1 || group == 2);
+}
+
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
+  PrefillKernelArgs p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.q_stride = a.q_stride;
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.k_stride = a.k_stride;
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.v_stride = a.v_stride;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.bt = a.block_tables;
+  p.max_blocks = a.max_blocks;
+  p.bs = a.block_size;
+  p.bs_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz(unsigned(a.block_size)) : -1;
+  p.num_blocks = a.num_blocks;
+  p.num_k_rows = a.num_k_rows;
+  p.num_q_tokens = a.num_q_tokens;
+  p.num_q_heads = a.num_q_heads;
+  p.num_kv_heads = a.num_kv_heads;
+  p.scale_log2 = a.scale * kLog2e;
+  p.causal = a.causal;
+  p.max_tiles = (a.max_seqlen_q + BM - 1) / BM;
+  p.out = static_cast<uint16_t*>(a.out);
+  if (p.max_tiles > 65535) return hipErrorInvalidConfiguration;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  return group == 1 ? launch_g<1>(p, a.batch, stream) : launch_g<2>(p, a.batch, stream);
+}
 
 }  // namespace pkv

@@ -11,17 +11,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 pkv_bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float pkv_f32x2_t;
 
+// float32 -> bf16 with the hardware converter (v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const pkv_f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, pkv_bf16x2_t));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return uint16_t(pack_bf16x2(f, 0.f) & 0xffffu); }
 
 // Element load/store as float for the generic kernels.
 template <typename T> struct Elem;
