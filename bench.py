@@ -277,6 +277,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode"], default=None,
+                    help="run just one secondary workload (after the headline), e.g. for a profiler")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -303,29 +305,39 @@ def main():
 
     secondary = {}
     if not args.headline_only:
-        log("prefill, workload 3")
-        p3 = bench_prefill(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers, paged=False)
-        log("prefix prefill, workload 4")
-        p4 = bench_prefill(pkv, torch, workloads.workload4, args.steps, args.warmup, args.layers, paged=True)
-        log("store sweep, workload 5")
-        st = bench_store(pkv, torch, args.steps, args.warmup)
-        log("long padded decode, workload 5")
-        d5 = bench_decode(pkv, torch, workloads.workload5_decode, max(args.steps // 5, 3), 2, 2)
+        want = lambda name: args.only in (None, name)
+        p3 = p4 = st = d5 = None
+        if want("prefill"):
+            log("prefill, workload 3")
+            p3 = bench_prefill(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers, paged=False)
+        if want("prefix"):
+            log("prefix prefill, workload 4")
+            p4 = bench_prefill(pkv, torch, workloads.workload4, args.steps, args.warmup, args.layers, paged=True)
+        if want("store"):
+            log("store sweep, workload 5")
+            st = bench_store(pkv, torch, args.steps, args.warmup)
+        if want("long_decode"):
+            log("long padded decode, workload 5")
+            d5 = bench_decode(pkv, torch, workloads.workload5_decode, max(args.steps // 5, 3), 2, 2)
         for name, r in (("varlen_prefill_workload3", p3), ("prefix_prefill_workload4", p4)):
+            if r is None:
+                continue
             tf = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
             secondary[name] = {"value": round(tf, 2), "unit": "TFLOP/s", "frac_bf16_mfma_peak":
                                round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "kernel_ms": round(r["kernel_ms"], 4),
                                "step_ms": round(r["wall_ms"], 4), "flops": r["flops"], "tokens": r["tokens"]}
-        gbs = st["bytes"] / (st["kernel_ms"] * 1e-3) / 1e9
-        secondary["store_sweep_workload5"] = {"value": round(gbs, 1), "unit": "GB/s",
-                                             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                             "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
-                                             "tokens": st["tokens"]}
-        gbs5 = d5["kv_bytes"] / (d5["kernel_ms"] * 1e-3) / 1e9
-        secondary["long_decode_workload5"] = {"value": round(gbs5, 1), "unit": "GB/s",
-                                             "frac_hbm_peak": round(gbs5 / HBM_PEAK_GBS, 4),
-                                             "kernel_ms": round(d5["kernel_ms"], 4), "kv_bytes": d5["kv_bytes"],
-                                             "step_ms": round(d5["wall_ms"], 4)}
+        if st is not None:
+            gbs = st["bytes"] / (st["kernel_ms"] * 1e-3) / 1e9
+            secondary["store_sweep_workload5"] = {"value": round(gbs, 1), "unit": "GB/s",
+                                                 "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                                 "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
+                                                 "tokens": st["tokens"]}
+        if d5 is not None:
+            gbs5 = d5["kv_bytes"] / (d5["kernel_ms"] * 1e-3) / 1e9
+            secondary["long_decode_workload5"] = {"value": round(gbs5, 1), "unit": "GB/s",
+                                                 "frac_hbm_peak": round(gbs5 / HBM_PEAK_GBS, 4),
+                                                 "kernel_ms": round(d5["kernel_ms"], 4), "kv_bytes": d5["kv_bytes"],
+                                                 "step_ms": round(d5["wall_ms"], 4)}
 
     cpu = None
     if not args.no_cpu:

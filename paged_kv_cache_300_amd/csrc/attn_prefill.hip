@@ -34,19 +34,43 @@ constexpr int HD = 128;
 constexpr int BM = 64;        // query tokens per work-group
 constexpr int BN = 64;        // keys per tile
 constexpr int THREADS = 256;  // 4 waves x 16 tokens
-constexpr int LROW = HD + 8;  // LDS row pitch in elements (272 bytes)
+// LDS row pitches (elements).  K rows are read 16 rows x 16 B per quarter-wave: a pitch of 272 B puts the
+// 16 reads on distinct banks.  V rows are read 4 rows x 32 B per quarter-wave by the transposing read: a
+// pitch of 288 B (32 B apart modulo 256 B) does the same for them.
+constexpr int KROW = HD + 8;
+constexpr int VROW = HD + 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMinusBig = -1e30f;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
-__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4& a, const u32x4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+
+// Transposing LDS read (gfx950): within each 16-lane quarter-wave, result lane i element j comes from the
+// 8 bytes addressed by source lane 4 j + i / 4, element i % 4.
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* lds_ptr) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(lds_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Maximum over lanes i and i ^ 16 (rows of 16 swapped pairwise), and over lanes i and i ^ 32.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 struct PrefillKernelArgs {
   const uint16_t* q;
@@ -72,6 +96,66 @@ struct PrefillKernelArgs {
   uint16_t* out;
 };
 
+struct TileSource {
+  const uint16_t* kbase;  // this thread's chunk of kv head `kvh` at slot/row 0
+  const uint16_t* vbase;
+  const int32_t* bt_row;  // null: contiguous rows
+  int krow;
+  int Lk;
+  int64_t k_start;
+  int64_t slot_elems;
+};
+
+struct Staged {
+  u32x4 k[4], v[4];
+};
+
+__device__ __forceinline__ int block_of(const PrefillKernelArgs& p, const int32_t* bt_row, int lb) {
+  const int blk = bt_row[lb];
+  return (blk >= 0 && blk < p.num_blocks) ? blk : 0;
+}
+
+__device__ __forceinline__ Staged load_tile(const PrefillKernelArgs& p, const TileSource& s, int kt) {
+  Staged r;
+  if (s.bt_row) {
+    const bool tile_in_block = p.bs_shift >= 6;
+    const int ublk = tile_in_block ? block_of(p, s.bt_row, (kt * BN) >> p.bs_shift) : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(kt * BN + s.krow + 16 * i, s.Lk - 1);
+      int64_t slot;
+      if (tile_in_block) {
+        slot = int64_t(ublk) * p.bs + (key & (p.bs - 1));
+      } else if (p.bs_shift >= 0) {
+        slot = int64_t(block_of(p, s.bt_row, key >> p.bs_shift)) * p.bs + (key & (p.bs - 1));
+      } else {
+        const int lb = key / p.bs;
+        slot = int64_t(block_of(p, s.bt_row, lb)) * p.bs + (key - lb * p.bs);
+      }
+      r.k[i] = *reinterpret_cast<const u32x4*>(s.kbase + slot * s.slot_elems);
+      r.v[i] = *reinterpret_cast<const u32x4*>(s.vbase + slot * s.slot_elems);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(kt * BN + s.krow + 16 * i, s.Lk - 1);
+      const int64_t row = min(max(s.k_start + key, int64_t(0)), p.num_k_rows - 1);
+      r.k[i] = *reinterpret_cast<const u32x4*>(s.kbase + row * p.k_stride);
+      r.v[i] = *reinterpret_cast<const u32x4*>(s.vbase + row * p.v_stride);
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ void store_tile(const Staged& st, uint16_t* lk, uint16_t* lv, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    *reinterpret_cast<u32x4*>(&lk[row * KROW + (tid & 15) * 8]) = st.k[i];
+    *reinterpret_cast<u32x4*>(&lv[row * VROW + (tid & 15) * 8]) = st.v[i];
+  }
+}
+
 template <int G>
 __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p) {
   const int kvh = blockIdx.x, b = blockIdx.y;
@@ -88,62 +172,45 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
   kend = max(kend, 0);
   const int n_tiles = (kend + BN - 1) / BN;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * LROW];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * VROW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int tok = t0 + wave * 16 + col;  // this lane's query token (column of every MFMA block)
   const int qpos = Lk - Lq + tok;
 
-  // Q^T operands: head n of the group, dims 32*ks + 8*grp .. +8.
-  uint4 qreg[G][4];
+  // Q^T operands: head n of the group, dims 32*ks + 8*grp .. +8.  A negative scale is carried by q's sign
+  // bits (exact in bf16), so the scale applied to the scores is c = |scale| * log2(e).
+  const float c = fabsf(p.scale_log2);
+  const uint32_t sign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  u32x4 qreg[G][4];
   {
     const bool ok = tok < Lq && q_start + tok < p.num_q_tokens;
     const uint16_t* qrow = p.q + int64_t(q_start + tok) * p.q_stride + int64_t(kvh) * G * HD + grp * 8;
 #pragma unroll
     for (int n = 0; n < G; ++n)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qreg[n][ks] = ok ? *reinterpret_cast<const uint4*>(qrow + n * HD + ks * 32) : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qrow + n * HD + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+        x.x ^= sign; x.y ^= sign; x.z ^= sign; x.w ^= sign;
+        qreg[n][ks] = x;
+      }
   }
 
-  // Staging: thread t moves 16-byte chunks c = t + 256 i (i < 4) of the K and V tiles: key c / 16, chunk c % 16.
-  uint4 kst[4], vst[4];
-  const int64_t slot_elems = int64_t(p.num_kv_heads) * HD;
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + THREADS * i;
-      const int key = kt * BN + (c >> 4);
-      const int ch = c & 15;
-      int64_t koff = -1, voff = -1;
-      if (key < Lk) {
-        if (p.bt) {
-          int lb, cell;
-          if (p.bs_shift >= 0) { lb = key >> p.bs_shift; cell = key & (p.bs - 1); }
-          else { lb = key / p.bs; cell = key - lb * p.bs; }
-          const int blk = p.bt[int64_t(b) * p.max_blocks + lb];
-          if (blk >= 0 && blk < p.num_blocks) koff = voff = (int64_t(blk) * p.bs + cell) * slot_elems;
-        } else if (k_start + key >= 0 && k_start + key < p.num_k_rows) {
-          koff = (k_start + key) * p.k_stride;
-          voff = (k_start + key) * p.v_stride;
-        }
-      }
-      const int64_t e = int64_t(kvh) * HD + ch * 8;
-      kst[i] = koff >= 0 ? *reinterpret_cast<const uint4*>(p.k + koff + e) : make_uint4(0, 0, 0, 0);
-      vst[i] = voff >= 0 ? *reinterpret_cast<const uint4*>(p.v + voff + e) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + THREADS * i;
-      const int off = (c >> 4) * LROW + (c & 15) * 8;
-      *reinterpret_cast<uint4*>(&lds_k[buf][off]) = kst[i];
-      *reinterpret_cast<uint4*>(&lds_v[buf][off]) = vst[i];
-    }
-  };
+  // Staging: thread t moves the 16-byte chunk (t % 16) of key rows t / 16 + 16 i (i < 4) of the K and V tiles.
+  // Keys past the end of the sequence read its last key instead (finite data; their scores are masked and
+  // their weights are exactly 0), so the loads need no branches.  In paged mode with block_size a multiple
+  // of 64 a whole tile lies in one block: one uniform block-table read per tile.
+  TileSource src;
+  src.kbase = p.k + int64_t(kvh) * HD + (tid & 15) * 8;
+  src.vbase = p.v + int64_t(kvh) * HD + (tid & 15) * 8;
+  src.bt_row = p.bt ? p.bt + int64_t(b) * p.max_blocks : nullptr;
+  src.krow = tid >> 4;
+  src.Lk = Lk;
+  src.k_start = k_start;
+  src.slot_elems = int64_t(p.num_kv_heads) * HD;
+  Staged st;
 
   f32x4_t o[8][G];
   float m[G], l[G];
@@ -156,14 +223,14 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
   }
 
   if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    st = load_tile(p, src, 0);
+    store_tile(st, lds_k[0], lds_v[0], tid);
   }
   __syncthreads();
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_tiles) load_tile(kt + 1);
+    if (kt + 1 < n_tiles) st = load_tile(p, src, kt + 1);
 
     // S^T = K Q^T for 4 blocks of 16 keys.
     f32x4_t s[4][G];
@@ -175,15 +242,18 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&lds_k[buf][(kb * 16 + col) * LROW + ks * 32 + grp * 8]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&lds_k[buf][(kb * 16 + col) * KROW + ks * 32 + grp * 8]);
 #pragma unroll
         for (int n = 0; n < G; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
       }
     }
 
-    // Scale, mask, online softmax.  Lane holds keys kt*64 + 16 kb + 4 grp + r of query `tok`.
+    // Mask, online softmax.  Lane holds raw scores of keys kt*64 + 16 kb + 4 grp + r for query `tok`; the
+    // scale c > 0 is applied inside exp2(s c - m) (q carries the sign of the scale), m is in scaled units.
     const bool need_mask = (kt + 1) * BN > Lk || (p.causal && (kt + 1) * BN - 1 > qpos0);
-    uint4 pb[G][2];
+    u32x4 pb[G][2];
+    bool grew = false;
+    float alpha[G];
 #pragma unroll
     for (int n = 0; n < G; ++n) {
       float mx = -INFINITY;
@@ -191,19 +261,19 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = s[kb][n][r] * p.scale_log2;
+          float x = s[kb][n][r];
           if (need_mask) {
             const int kp = kt * BN + kb * 16 + grp * 4 + r;
             const bool vis = kp < Lk && (!p.causal || kp <= qpos);
             x = vis ? x : -INFINITY;
+            s[kb][n][r] = x;
           }
-          s[kb][n][r] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, shfl_xor_f32(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-      const float mn = fmaxf(m[n], mx);
-      const float alpha = fast_exp2(m[n] - mn);
+      mx = max_xor32(max_xor16(mx));
+      const float mn = fmaxf(m[n], mx * c);
+      alpha[n] = fast_exp2(m[n] - mn);
+      grew |= mn > m[n];
       m[n] = mn;
       float sum = 0.f;
       float pv[4][4];
@@ -211,12 +281,10 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pv[kb][r] = fast_exp2(s[kb][n][r] - mn);
+          pv[kb][r] = fast_exp2(fmaf(s[kb][n][r], c, -mn));
           sum += pv[kb][r];
         }
-      l[n] = l[n] * alpha + sum;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[d][n] *= alpha;
+      l[n] = fmaf(l[n], alpha[n], sum);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         pb[n][h].x = pack_bf16x2(pv[2 * h][0], pv[2 * h][1]);
@@ -225,26 +293,33 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
         pb[n][h].w = pack_bf16x2(pv[2 * h + 1][2], pv[2 * h + 1][3]);
       }
     }
+    // Rescale the output only when some running maximum of the wave moved (rare after the first tiles).
+    if (__any(grew)) {
+#pragma unroll
+      for (int n = 0; n < G; ++n)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[d][n] *= alpha[n];
+    }
 
-    // O^T += V^T P^T: A operand = V^T rows (dims), k slots = keys {4 grp + r} and {16 + 4 grp + r} of each
-    // 32-key half, matching the P^T slots filled above.
+    // O^T += V^T P^T.  A operand = V^T: lane (col, grp) needs V[key][16 d + col] for the keys of its P^T slots,
+    // {4 grp + j} and {16 + 4 grp + j} (j < 4) of each 32-key half.  ds_read_b64_tr_b16 transposes 16x4 blocks
+    // inside each quarter-wave: source lane 4 j + q supplies V[key j][dim0 + 4 q .. + 3] and result lane i
+    // receives V[key j][dim0 + i] for j = 0..3.
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint16_t* vb = &lds_v[buf][(h * 32 + grp * 4) * LROW];
+      const int row = h * 32 + grp * 4 + (col >> 2);
+      const uint16_t* vrow = &lds_v[buf][row * VROW + (col & 3) * 4];
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const int dim = d * 16 + col;
-        uint4 a;
-        a.x = uint32_t(vb[0 * LROW + dim]) | (uint32_t(vb[1 * LROW + dim]) << 16);
-        a.y = uint32_t(vb[2 * LROW + dim]) | (uint32_t(vb[3 * LROW + dim]) << 16);
-        a.z = uint32_t(vb[16 * LROW + dim]) | (uint32_t(vb[17 * LROW + dim]) << 16);
-        a.w = uint32_t(vb[18 * LROW + dim]) | (uint32_t(vb[19 * LROW + dim]) << 16);
+        const u32x2 lo = ds_read_tr16(vrow + d * 16);
+        const u32x2 hi = ds_read_tr16(vrow + 16 * VROW + d * 16);
+        const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int n = 0; n < G; ++n) o[d][n] = mfma_16x16x32(a, pb[n][h], o[d][n]);
       }
     }
 
-    if (kt + 1 < n_tiles) store_tile(buf ^ 1);
+    if (kt + 1 < n_tiles) store_tile(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
     __syncthreads();
   }
 
@@ -263,10 +338,10 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
       uint16_t* orow = p.out + (int64_t(q_start + tok) * p.num_q_heads + kvh * G + n) * HD + grp * 4;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        uint2 w;
+        u32x2 w;
         w.x = pack_bf16x2(o[d][n][0] * inv[n], o[d][n][1] * inv[n]);
         w.y = pack_bf16x2(o[d][n][2] * inv[n], o[d][n][3] * inv[n]);
-        *reinterpret_cast<uint2*>(orow + d * 16) = w;
+        *reinterpret_cast<u32x2*>(orow + d * 16) = w;
       }
     }
   }

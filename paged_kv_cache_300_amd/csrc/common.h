@@ -11,6 +11,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Plain clang vector types: unlike HIP's uint4 class they load and store as one register tuple and never
+// force a copy through private memory.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 pkv_bf16x2_t;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float pkv_f32x2_t;
 
