@@ -6,22 +6,27 @@
 // h / (Hq / Hkv) [P2 §3].
 //
 // How (gfx950 design, not the pages' library call):
-//  * Split-KV: a work-group owns one (sequence, kv head, split of `split_tokens` keys) and serves every
-//    query head of that kv head's GQA group, so each K/V row is read from HBM once for the whole group.
-//    Short and long contexts alike become many equal-sized work-groups, which keeps all 256 CUs busy.
+//  * Even split of the whole batch: the keys of all sequences, laid end to end (T = sum of context
+//    lengths), are cut into W equal ranges, one per worker, with W x (kv-head groups) = the number of
+//    work-groups the 256 CUs hold at once.  Every work-group therefore streams the same number of bytes and the launch is a
+//    single round with no tail, whatever the mix of context lengths (a range may cover the end of one
+//    sequence and the start of the next).
+//  * A work-group has one wave per kv head, so together its waves read whole contiguous token rows of the
+//    cache; each wave serves every query head of its kv head's GQA group, so each K/V row is read from HBM
+//    once for the whole group.
 //  * A token's 256-byte K (or V) row for one kv head is read by 8 lanes, 2 x 16 bytes each; a wave reads
 //    8 tokens per instruction (8 full 128-byte lines) and 32 tokens per iteration, all loads issued before
-//    any arithmetic so 16 KiB per wave are in flight.  The block-table entries a split touches are staged
-//    once in LDS.
+//    any arithmetic; the block-table entries of the next iteration are fetched one iteration ahead.
 //  * q.k uses the packed bf16 dot instruction (exact products, float32 sums); the 8 partial sums of a
 //    token are combined with three DPP moves inside the 8-lane group.
 //  * Each 8-lane group runs its own online softmax (running max m, normaliser l, unnormalised output) over
-//    its tokens [P2 §5.2 ②], in base 2 with log2(e) folded into the scale.  At the end the 8 groups of a wave
-//    are merged with lane shuffles, the 4 waves through LDS, and splits by a second small kernel -- every
-//    merge is the same exact rescaling by exp(m_i - m).
-//  * A sequence that fits in one split writes its output directly; longer ones write (m, l, unnormalised
-//    output) per split to the workspace for the combine kernel.
+//    its tokens [P2 §5.2 ②], in base 2 with log2(e) folded into the scale.  At the end of a sequence's
+//    range the 8 groups are merged with lane shuffles; a sequence wholly inside one range is written
+//    directly, otherwise each range writes (m, l, unnormalised output) and a combine kernel merges them with
+//    the same exact rescaling by exp(m_i - m).
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "launch.h"
@@ -30,9 +35,10 @@ namespace pkv {
 namespace {
 
 constexpr int HD = 128;
-constexpr int THREADS = 256;  // 4 waves
+constexpr int MAX_WAVES = 4;  // kv heads per work-group, one wave each
 constexpr int WAVE_TOKENS = 32;
-constexpr int WG_TOKENS = 4 * WAVE_TOKENS;
+constexpr int MAX_WORKERS = 1024;  // upper bound of W, used to size the workspace
+constexpr int LDS_CU_MAX = 2048;   // prefix sums staged in LDS up to this many entries
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMinusBig = -1e30f;  // finite "no key yet" maximum, so exp2(m_old - m_new) never sees inf - inf
 
@@ -52,234 +58,355 @@ struct DecodeKernelArgs {
   int num_blocks;
   const int32_t* ctx;
   const int32_t* bt;
+  int batch;
   int max_blocks;
   int bs;
   int bs_shift;  // log2(block_size) when it is a power of two, else -1
   int num_q_heads;
   int num_kv_heads;
   float scale_log2;
-  int split_tokens;
-  int max_splits;
+  int workers;     // W
+  int64_t* cu;     // [batch + 1] prefix sums of the clamped context lengths (workspace)
+  float* ws_acc;   // [W + batch][Hq][HD] unnormalised partial outputs (workspace)
+  float* ws_ml;    // [W + batch][Hq][2] partial (m, l) (workspace)
   uint16_t* out;
-  float* ws_acc;  // [B][Hq][max_splits][HD]
-  float* ws_ml;   // [B][Hq][max_splits][2]
 };
 
-template <int G>
-__global__ void __launch_bounds__(THREADS) decode_split_kernel(DecodeKernelArgs p) {
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int ctx = min(p.ctx[b], p.max_blocks * p.bs);
-  const int t0 = split * p.split_tokens;
-  if (t0 >= ctx) return;  // whole work-group: this split is past the end of the context
-  const int t1 = min(ctx, t0 + p.split_tokens);
-  const int nsplit = (ctx + p.split_tokens - 1) / p.split_tokens;
+__device__ __forceinline__ int clamp_ctx(const DecodeKernelArgs& p, int b) {
+  return min(max(p.ctx[b], 0), p.max_blocks * p.bs);
+}
 
-  extern __shared__ int s_blk[];  // block-table entries of the logical blocks [t0, t1) touches
-  __shared__ float s_acc[4][G][HD];
-  __shared__ float s_m[4][G], s_l[4][G];
-
-  const int bs = p.bs;
-  const int first_lb = t0 / bs;
-  const int nlb = (t1 - 1) / bs - first_lb + 1;
-  const int32_t* bt_row = p.bt + int64_t(b) * p.max_blocks;
-  for (int i = threadIdx.x; i < nlb; i += THREADS) {
-    const int blk = bt_row[first_lb + i];
-    s_blk[i] = (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+// Prefix sums of the clamped context lengths: cu[b] = sum_{i<b} ctx_i.  One work-group of 1024 threads.
+__global__ void __launch_bounds__(1024) decode_prefix_kernel(DecodeKernelArgs p) {
+  __shared__ int64_t part[1024];
+  __shared__ int64_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < p.batch; base += 1024) {
+    const int b = base + threadIdx.x;
+    const int64_t x = b < p.batch ? clamp_ctx(p, b) : 0;
+    part[threadIdx.x] = x;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan
+      const int64_t y = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+      __syncthreads();
+      part[threadIdx.x] += y;
+      __syncthreads();
+    }
+    if (b < p.batch) p.cu[b] = carry + part[threadIdx.x] - x;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += part[1023];
+    __syncthreads();
   }
+  if (threadIdx.x == 0) p.cu[p.batch] = carry;
+}
+
+__device__ __forceinline__ int64_t range_begin(int64_t T, int W, int w) { return T * w / W; }
+
+// The worker whose range holds global key index x (ranges are [range_begin(w), range_begin(w + 1))).
+__device__ __forceinline__ int worker_of(int64_t T, int W, int64_t x) { return int(((x + 1) * W - 1) / T); }
+
+template <int G>
+__global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKernelArgs p) {
+  const int w = blockIdx.y, W = p.workers;
+  const int64_t T = p.cu[p.batch];
+  int64_t x = range_begin(T, W, w);
+  const int64_t x_end = range_begin(T, W, w + 1);
+  if (x >= x_end) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kvh = blockIdx.x * (blockDim.x >> 6) + wave;
   const int grp = lane >> 3, sub = lane & 7;
-
-  // This lane's 16 query dims (sub*8 .. +8 and 64 + sub*8 .. +8) of each head in the group, as bf16 pairs.
-  uint32_t qa[G][4], qb[G][4];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint16_t* qp = p.q + int64_t(b) * p.q_stride + (kvh * G + g) * HD + sub * 8;
-    const uint4 x = *reinterpret_cast<const uint4*>(qp);
-    const uint4 y = *reinterpret_cast<const uint4*>(qp + 64);
-    qa[g][0] = x.x; qa[g][1] = x.y; qa[g][2] = x.z; qa[g][3] = x.w;
-    qb[g][0] = y.x; qb[g][1] = y.y; qb[g][2] = y.z; qb[g][3] = y.w;
-  }
-  __syncthreads();
-
-  float m[G], l[G], acc[G][16];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kMinusBig;
-    l[g] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
-  }
-
+  const int bs = p.bs;
   const int64_t slot_elems = int64_t(p.num_kv_heads) * HD;
   const uint16_t* kbase = p.kc + kvh * HD + sub * 8;
   const uint16_t* vbase = p.vc + kvh * HD + sub * 8;
 
-  for (int base = t0 + wave * WAVE_TOKENS; base < t1; base += WG_TOKENS) {
-    uint4 ka[4], kb[4], va[4], vb[4];
-    bool ok[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = base + u * 8 + grp;
-      bool valid = t < t1;
-      const int tt = valid ? t : t0;
-      int lb, cell;
-      if (p.bs_shift >= 0) {
-        lb = tt >> p.bs_shift;
-        cell = tt & (bs - 1);
-      } else {
-        lb = tt / bs;
-        cell = tt - lb * bs;
-      }
-      const int blk = s_blk[lb - first_lb];
-      // A key past the split reads the split's first key instead (a real, finite row): its weight is 0, and
-      // 0 * (stale or poisoned data) could be NaN.  Only an unusable block-table entry falls back to slot 0.
-      const int64_t off = blk >= 0 ? (int64_t(blk) * bs + cell) * slot_elems : 0;
-      ok[u] = valid && blk >= 0;
-      ka[u] = *reinterpret_cast<const uint4*>(kbase + off);
-      kb[u] = *reinterpret_cast<const uint4*>(kbase + off + 64);
-      va[u] = *reinterpret_cast<const uint4*>(vbase + off);
-      vb[u] = *reinterpret_cast<const uint4*>(vbase + off + 64);
+  // First sequence of the range: the last b with cu[b] <= x (empty sequences are skipped over).  The prefix
+  // sums are staged in LDS when they fit, so the search costs one global round trip instead of log2(batch).
+  extern __shared__ int64_t s_cu[];
+  const bool cu_in_lds = p.batch + 1 <= LDS_CU_MAX;
+  if (cu_in_lds) {
+    for (int i = threadIdx.x; i <= p.batch; i += blockDim.x) s_cu[i] = p.cu[i];
+    __syncthreads();
+  }
+  int b;
+  {
+    int lo = 0, hi = p.batch;  // cu[lo] <= x < cu[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((cu_in_lds ? s_cu[mid] : p.cu[mid]) <= x) lo = mid; else hi = mid;
     }
+    b = lo;
+  }
+  if (kvh >= p.num_kv_heads) return;
 
-    float pr[4][G];
+  while (x < x_end && b < p.batch) {
+    const int64_t seq0 = cu_in_lds ? s_cu[b] : p.cu[b];
+    const int64_t seq1 = cu_in_lds ? s_cu[b + 1] : p.cu[b + 1];
+    if (seq1 <= x) {  // empty sequence
+      ++b;
+      continue;
+    }
+    const int ctx = int(seq1 - seq0);
+    const int t0 = int(x - seq0);
+    const int t1 = int(min(x_end, seq1) - seq0);
+    const int32_t* bt_row = p.bt + int64_t(b) * p.max_blocks;
+
+    // This lane's 16 query dims (sub*8 .. +8 and 64 + sub*8 .. +8) of each head in the group, as bf16 pairs.
+    uint32_t qa[G][4], qb[G][4];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float s[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float d = 0.f;
-        d = dot2(qa[g][0], ka[u].x, d);
-        d = dot2(qa[g][1], ka[u].y, d);
-        d = dot2(qa[g][2], ka[u].z, d);
-        d = dot2(qa[g][3], ka[u].w, d);
-        d = dot2(qb[g][0], kb[u].x, d);
-        d = dot2(qb[g][1], kb[u].y, d);
-        d = dot2(qb[g][2], kb[u].z, d);
-        d = dot2(qb[g][3], kb[u].w, d);
-        d = sum8(d);
-        s[u] = ok[u] ? d * p.scale_log2 : -INFINITY;
-      }
-      const float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      const float mn = fmaxf(m[g], mx);
-      const float alpha = fast_exp2(m[g] - mn);
-      float sum = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        pr[u][g] = fast_exp2(s[u] - mn);
-        sum += pr[u][g];
-      }
-      l[g] = l[g] * alpha + sum;
-      m[g] = mn;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[g][i] *= alpha;
+      const uint16_t* qp = p.q + int64_t(b) * p.q_stride + (kvh * G + g) * HD + sub * 8;
+      const u32x4 xq = *reinterpret_cast<const u32x4*>(qp);
+      const u32x4 yq = *reinterpret_cast<const u32x4*>(qp + 64);
+      qa[g][0] = xq.x; qa[g][1] = xq.y; qa[g][2] = xq.z; qa[g][3] = xq.w;
+      qb[g][0] = yq.x; qb[g][1] = yq.y; qb[g][2] = yq.z; qb[g][3] = yq.w;
     }
 
+    float m[G], l[G], acc[G][16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t w[8] = {va[u].x, va[u].y, va[u].z, va[u].w, vb[u].x, vb[u].y, vb[u].z, vb[u].w};
-      float vf[16];
+    for (int g = 0; g < G; ++g) {
+      m[g] = kMinusBig;
+      l[g] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        vf[2 * i] = bf16_lo(w[i]);
-        vf[2 * i + 1] = bf16_hi(w[i]);
+      for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
+    }
+
+    // Slot of this lane's token u in the iteration starting at `base` (token base + 8 u + grp).  A token
+    // past the range reads the range's first token instead (a real, finite row whose weight is 0, where
+    // 0 * stale or poisoned data could be NaN); an unusable block-table entry reads slot 0 and is masked.
+    int64_t slot_n[4];
+    bool ok_n[4];
+    auto locate = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = base + u * 8 + grp;
+        const int tt = t < t1 ? t : t0;
+        int lb, cell;
+        if (p.bs_shift >= 0) {
+          lb = tt >> p.bs_shift;
+          cell = tt & (bs - 1);
+        } else {
+          lb = tt / bs;
+          cell = tt - lb * bs;
+        }
+        const int blk = bt_row[lb];
+        const bool usable = blk >= 0 && blk < p.num_blocks;
+        ok_n[u] = usable && t < t1;
+        slot_n[u] = usable ? int64_t(blk) * bs + cell : 0;
       }
+    };
+    locate(t0);
+
+    for (int base = t0; base < t1; base += WAVE_TOKENS) {
+      u32x4 ka[4], kb[4], va[4], vb[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t off = slot_n[u] * slot_elems;
+        ok[u] = ok_n[u];
+        ka[u] = *reinterpret_cast<const u32x4*>(kbase + off);
+        kb[u] = *reinterpret_cast<const u32x4*>(kbase + off + 64);
+        va[u] = *reinterpret_cast<const u32x4*>(vbase + off);
+        vb[u] = *reinterpret_cast<const u32x4*>(vbase + off + 64);
+      }
+      if (base + WAVE_TOKENS < t1) locate(base + WAVE_TOKENS);
+
+      float pr[4][G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        float s[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[g][i] = fmaf(pr[u][g], vf[i], acc[g][i]);
+        for (int u = 0; u < 4; ++u) {
+          float d = 0.f;
+          d = dot2(qa[g][0], ka[u].x, d);
+          d = dot2(qa[g][1], ka[u].y, d);
+          d = dot2(qa[g][2], ka[u].z, d);
+          d = dot2(qa[g][3], ka[u].w, d);
+          d = dot2(qb[g][0], kb[u].x, d);
+          d = dot2(qb[g][1], kb[u].y, d);
+          d = dot2(qb[g][2], kb[u].z, d);
+          d = dot2(qb[g][3], kb[u].w, d);
+          d = sum8(d);
+          s[u] = ok[u] ? d * p.scale_log2 : -INFINITY;
+        }
+        const float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        const float mn = fmaxf(m[g], mx);
+        const float alpha = fast_exp2(m[g] - mn);
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          pr[u][g] = fast_exp2(s[u] - mn);
+          sum += pr[u][g];
+        }
+        l[g] = l[g] * alpha + sum;
+        m[g] = mn;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] *= alpha;
       }
-    }
-  }
 
-  // Merge the 8 lane groups of the wave (lanes with equal `sub` hold the same dims).
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t wv[8] = {va[u].x, va[u].y, va[u].z, va[u].w, vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+        float vf[16];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = shfl_xor_f32(m[g], off);
-      const float lo = shfl_xor_f32(l[g], off);
-      const float mn = fmaxf(m[g], mo);
-      const float a = fast_exp2(m[g] - mn), c = fast_exp2(mo - mn);
-      l[g] = l[g] * a + lo * c;
-      m[g] = mn;
+        for (int i = 0; i < 8; ++i) {
+          vf[2 * i] = bf16_lo(wv[i]);
+          vf[2 * i + 1] = bf16_hi(wv[i]);
+        }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[g][i] = acc[g][i] * a + shfl_xor_f32(acc[g][i], off) * c;
-    }
-  }
-  if (grp == 0) {
+        for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        s_acc[wave][g][sub * 8 + i] = acc[g][i];
-        s_acc[wave][g][64 + sub * 8 + i] = acc[g][8 + i];
-      }
-      if (sub == 0) {
-        s_m[wave][g] = m[g];
-        s_l[wave][g] = l[g];
+          for (int i = 0; i < 16; ++i) acc[g][i] = fmaf(pr[u][g], vf[i], acc[g][i]);
+        }
       }
     }
-  }
-  __syncthreads();
 
-  // Merge the 4 waves; one thread per (head of the group, dim).
-  for (int idx = threadIdx.x; idx < G * HD; idx += THREADS) {
-    const int g = idx / HD, d = idx % HD;
-    float M = s_m[0][g];
+    // Merge the 8 lane groups of the wave (lanes with equal `sub` hold the same dims).
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][g]);
-    float L = 0.f, A = 0.f;
+    for (int off = 8; off < 64; off <<= 1) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float e = fast_exp2(s_m[w][g] - M);
-      L = fmaf(s_l[w][g], e, L);
-      A = fmaf(s_acc[w][g][d], e, A);
-    }
-    const int qh = kvh * G + g;
-    if (nsplit == 1) {
-      p.out[(int64_t(b) * p.num_q_heads + qh) * HD + d] = f32_to_bf16(L > 0.f ? A / L : 0.f);
-    } else {
-      const int64_t row = (int64_t(b) * p.num_q_heads + qh) * p.max_splits + split;
-      p.ws_acc[row * HD + d] = A;
-      if (d == 0) {
-        p.ws_ml[2 * row] = M;
-        p.ws_ml[2 * row + 1] = L;
+      for (int g = 0; g < G; ++g) {
+        const float mo = shfl_xor_f32(m[g], off);
+        const float lo = shfl_xor_f32(l[g], off);
+        const float mn = fmaxf(m[g], mo);
+        const float a = fast_exp2(m[g] - mn), c = fast_exp2(mo - mn);
+        l[g] = l[g] * a + lo * c;
+        m[g] = mn;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] = acc[g][i] * a + shfl_xor_f32(acc[g][i], off) * c;
       }
     }
+    // Lanes 0..7 hold the result: dims sub*8 .. +8 and 64 + sub*8 .. +8 of each head of the group.
+    if (grp == 0) {
+      const bool whole = t0 == 0 && t1 == ctx;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int qh = kvh * G + g;
+        if (whole) {
+          const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+          uint16_t* o = p.out + (int64_t(b) * p.num_q_heads + qh) * HD + sub * 8;
+          u32x4 lo4, hi4;
+          lo4.x = pack_bf16x2(acc[g][0] * inv, acc[g][1] * inv);
+          lo4.y = pack_bf16x2(acc[g][2] * inv, acc[g][3] * inv);
+          lo4.z = pack_bf16x2(acc[g][4] * inv, acc[g][5] * inv);
+          lo4.w = pack_bf16x2(acc[g][6] * inv, acc[g][7] * inv);
+          hi4.x = pack_bf16x2(acc[g][8] * inv, acc[g][9] * inv);
+          hi4.y = pack_bf16x2(acc[g][10] * inv, acc[g][11] * inv);
+          hi4.z = pack_bf16x2(acc[g][12] * inv, acc[g][13] * inv);
+          hi4.w = pack_bf16x2(acc[g][14] * inv, acc[g][15] * inv);
+          *reinterpret_cast<u32x4*>(o) = lo4;
+          *reinterpret_cast<u32x4*>(o + 64) = hi4;
+        } else {
+          // (worker, sequence) pairs that share keys are distinct in w + b: slot w + b holds this partial.
+          const int64_t row = int64_t(w + b) * p.num_q_heads + qh;
+          float* a = p.ws_acc + row * HD + sub * 8;
+          *reinterpret_cast<float4*>(a) = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+          *reinterpret_cast<float4*>(a + 4) = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
+          *reinterpret_cast<float4*>(a + 64) = make_float4(acc[g][8], acc[g][9], acc[g][10], acc[g][11]);
+          *reinterpret_cast<float4*>(a + 68) = make_float4(acc[g][12], acc[g][13], acc[g][14], acc[g][15]);
+          if (sub == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * row) = make_float2(m[g], l[g]);
+        }
+      }
+    }
+    x = seq0 + t1;
+    ++b;
   }
 }
 
-// One work-group of 128 threads per (query head, sequence): merge the splits' partial states.
-__global__ void __launch_bounds__(HD) decode_combine_kernel(const int32_t* __restrict__ ctx_lens, int max_ctx,
-                                                           int split_tokens, int max_splits, int num_q_heads,
-                                                           const float* __restrict__ ws_acc,
-                                                           const float* __restrict__ ws_ml, uint16_t* __restrict__ out) {
+// One work-group of 128 threads per (query head, sequence): merge the partial states of the workers whose
+// ranges cut the sequence, or write zeros for an empty context.  Partials are read 8 at a time (independent
+// loads in flight) and merged with a running maximum, the same exact rescaling as everywhere else.
+__global__ void __launch_bounds__(HD) decode_combine_kernel(DecodeKernelArgs p) {
   const int qh = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int ctx = min(ctx_lens[b], max_ctx);
-  uint16_t* o = out + (int64_t(b) * num_q_heads + qh) * HD + d;
-  if (ctx <= 0) {  // padding row or empty context: zeros
+  const int64_t T = p.cu[p.batch];
+  const int64_t x0 = p.cu[b], x1 = p.cu[b + 1];
+  uint16_t* o = p.out + (int64_t(b) * p.num_q_heads + qh) * HD + d;
+  if (x1 <= x0) {  // padding row or empty context: zeros
     *o = 0;
     return;
   }
-  const int n = (ctx + split_tokens - 1) / split_tokens;
-  if (n == 1) return;  // written by the split kernel
-  const int64_t row0 = (int64_t(b) * num_q_heads + qh) * max_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, ws_ml[2 * (row0 + s)]);
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const float e = fast_exp2(ws_ml[2 * (row0 + s)] - M);
-    L = fmaf(ws_ml[2 * (row0 + s) + 1], e, L);
-    A = fmaf(ws_acc[(row0 + s) * HD + d], e, A);
+  const int W = p.workers;
+  const int w0 = worker_of(T, W, x0), w1 = worker_of(T, W, x1 - 1);
+  if (w0 == w1) return;  // written by its worker
+  const bool dense = T >= W;  // then no range is empty
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  for (int c0 = w0; c0 <= w1; c0 += 8) {
+    float mv[8], lv[8], av[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int w = c0 + j;
+      const bool valid = w <= w1 && (dense || range_begin(T, W, w) < range_begin(T, W, w + 1));
+      const int64_t row = int64_t(w + b) * p.num_q_heads + qh;
+      const float2 ml = valid ? *reinterpret_cast<const float2*>(p.ws_ml + 2 * row) : make_float2(-INFINITY, 0.f);
+      mv[j] = ml.x;
+      lv[j] = ml.y;
+      av[j] = valid ? p.ws_acc[row * HD + d] : 0.f;
+    }
+    float cm = mv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cm = fmaxf(cm, mv[j]);
+    const float mn = fmaxf(M, cm);
+    const float sc = fast_exp2(M - mn);
+    L *= sc;
+    A *= sc;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e = fast_exp2(mv[j] - mn);
+      L = fmaf(lv[j], e, L);
+      A = fmaf(av[j], e, A);
+    }
+    M = mn;
   }
   *o = f32_to_bf16(L > 0.f ? A / L : 0.f);
 }
 
-template <int G>
-hipError_t launch_g(const DecodeKernelArgs& p, int batch, hipStream_t stream) {
-  const size_t lds = size_t((p.split_tokens - 1) / p.bs + 2) * sizeof(int);
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(p.max_splits, p.num_kv_heads, batch), dim3(THREADS), lds, stream, p);
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t cu, acc, ml, total;
+};
+
+Layout workspace_layout(int batch, int num_q_heads) {
+  Layout L;
+  const size_t slots = size_t(MAX_WORKERS) + size_t(batch);
+  L.cu = 0;
+  L.acc = align256(size_t(batch + 1) * sizeof(int64_t));
+  L.ml = L.acc + align256(slots * num_q_heads * HD * sizeof(float));
+  L.total = L.ml + align256(slots * num_q_heads * 2 * sizeof(float));
+  return L;
+}
+
+// W: as many work-groups as the device keeps resident at once (cached per device and kernel shape).
+int resident_workers(const void* kernel, int threads, int key) {
+  static int cached[64][3][MAX_WAVES + 1] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int& slot = cached[dev][key][threads / 64];
+  if (slot > 0) return slot;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, LDS_CU_MAX * sizeof(int64_t)) !=
+          hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  slot = std::min(MAX_WORKERS, cus * per_cu);
+  return slot;
+}
+
+template <int G, int KEY>
+hipError_t launch_g(DecodeKernelArgs& p, hipStream_t stream) {
+  const int waves = std::min(MAX_WAVES, p.num_kv_heads);
+  const int threads = 64 * waves;
+  const int head_groups = (p.num_kv_heads + waves - 1) / waves;
+  // One resident round in total: W workers x head_groups work-groups, the head groups of a worker adjacent
+  // in launch order so they read the two halves of the same token rows at the same time.
+  const int resident = resident_workers(reinterpret_cast<const void*>(&decode_lean_kernel<G>), threads, KEY);
+  p.workers = std::max(1, resident / head_groups);
+  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, p);
+  const size_t lds = p.batch + 1 <= LDS_CU_MAX ? size_t(p.batch + 1) * sizeof(int64_t) : 0;
+  hipLaunchKernelGGL(decode_lean_kernel<G>, dim3(head_groups, p.workers), dim3(threads), lds, stream, p);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.num_q_heads, p.batch), dim3(HD), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -289,23 +416,16 @@ bool decode_fast_supported(int head_dim, int group, bool bf16) {
   return bf16 && head_dim == HD && (group == 1 || group == 2 || group == 4);
 }
 
-DecodePlan decode_plan(int batch, int num_q_heads, int num_kv_heads, int max_ctx) {
-  // Enough work-groups to cover 256 CUs many times over at the longest context, without splits so short
-  // that the per-split partial state becomes a noticeable share of the traffic.
-  const int64_t units = int64_t(batch) * num_kv_heads;
-  int64_t want = units * int64_t(max_ctx) / 8192;
-  int split = 256;
-  while (split < want && split < 2048) split *= 2;
+DecodePlan decode_plan(int batch, int num_q_heads, int /*num_kv_heads*/, int /*max_ctx*/) {
   DecodePlan plan;
-  plan.split_tokens = split;
-  plan.max_splits = int((int64_t(max_ctx) + split - 1) / split);
-  plan.workspace_bytes = plan.max_splits > 1
-                             ? size_t(batch) * num_q_heads * plan.max_splits * (HD + 2) * sizeof(float)
-                             : 0;
+  plan.workspace_bytes = workspace_layout(batch, num_q_heads).total;
   return plan;
 }
 
 hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t stream) {
+  (void)plan;
+  const Layout L = workspace_layout(a.batch, a.num_q_heads);
+  char* ws = static_cast<char*>(workspace);
   DecodeKernelArgs p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.q_stride = a.q_stride;
@@ -314,28 +434,20 @@ hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* w
   p.num_blocks = a.num_blocks;
   p.ctx = a.ctx_lens;
   p.bt = a.block_tables;
+  p.batch = a.batch;
   p.max_blocks = a.max_blocks;
   p.bs = a.block_size;
   p.bs_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz(unsigned(a.block_size)) : -1;
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.scale_log2 = a.scale * kLog2e;
-  p.split_tokens = plan.split_tokens;
-  p.max_splits = plan.max_splits;
+  p.workers = 0;
+  p.cu = reinterpret_cast<int64_t*>(ws + L.cu);
+  p.ws_acc = reinterpret_cast<float*>(ws + L.acc);
+  p.ws_ml = reinterpret_cast<float*>(ws + L.ml);
   p.out = static_cast<uint16_t*>(a.out);
-  float* ws = static_cast<float*>(workspace);
-  const size_t acc_elems = size_t(a.batch) * a.num_q_heads * plan.max_splits * HD;
-  p.ws_acc = plan.max_splits > 1 ? ws : nullptr;
-  p.ws_ml = plan.max_splits > 1 ? ws + acc_elems : nullptr;
   const int group = a.num_q_heads / a.num_kv_heads;
-  hipError_t e = group == 1 ? launch_g<1>(p, a.batch, stream)
-                 : group == 2 ? launch_g<2>(p, a.batch, stream)
-                              : launch_g<4>(p, a.batch, stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.num_q_heads, a.batch), dim3(HD), 0, stream, a.ctx_lens,
-                     a.max_blocks * a.block_size, plan.split_tokens, plan.max_splits, a.num_q_heads, p.ws_acc, p.ws_ml,
-                     p.out);
-  return hipGetLastError();
+  return group == 1 ? launch_g<1, 0>(p, stream) : group == 2 ? launch_g<2, 1>(p, stream) : launch_g<4, 2>(p, stream);
 }
 
 }  // namespace pkv
