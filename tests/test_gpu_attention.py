@@ -91,6 +91,9 @@ DECODE_CASES = [
     ("bf16", 16, 4, 128, 1, [65, 200, 3], 14),
     ("bf16", 16, 2, 128, 32, [700, 33], 15),  # group of 8: generic path
     ("bf16", 8, 4, 64, 8, [100, 9, 513], 16),   # head_dim 64: generic path
+    ("bf16", 4, 2, 128, 16, [40, 0, 3, 77], 19),  # two kv heads: small work-groups
+    ("bf16", 16, 8, 128, 256, [0, 0, 0], 20),      # all padding: no key anywhere
+    ("bf16", 16, 8, 128, 4, [1, 2, 0], 30),        # fewer keys than work-groups: empty ranges
     ("f32", 4, 2, 16, 4, [1, 7, 30, 100], 17),
     ("f32", 16, 8, 128, 256, [300, 1], 18),
 ]
@@ -108,6 +111,20 @@ def test_decode_small(pkv, dtype, hq, hkv, hd, bs, ctx, seed):
     _check_attention(case, out)
     if 0 in ctx:
         assert bool((out[ctx.index(0)] == 0).all())
+
+
+def test_decode_batch_beyond_lds_prefix_staging(pkv):
+    """2100 sequences (more than the 2048 prefix sums the decode stages in LDS, more than one 1024-wide scan)."""
+    rng = np.random.default_rng(61)
+    ctx = rng.integers(0, 40, 2100)
+    case = workloads.decode_case(ctx, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=16,
+                                 num_blocks=int(sum(math.ceil(c / 16) for c in ctx)) + 1, seed=61, max_blocks=3)
+    log(f"decode batch {case.batch}, sum ctx {int(ctx.sum())}")
+    out, kc, vc, sm = _run_step(pkv, case, paged=True)
+    np.testing.assert_array_equal(to_host(sm), oracle_slot_mapping(case))
+    _check_attention(case, out, rows=list(range(0, 2100, 7)) + [2099])
+    zeros = np.where(ctx == 0)[0]
+    assert bool((out[torch.from_numpy(zeros).cuda()] == 0).all())
 
 
 PREFILL_CASES = [
