@@ -19,7 +19,8 @@
 //    loads are in flight while the current tile is multiplied; rows are padded (272 B) so the 16 lanes of a
 //    quarter-wave hit distinct banks.
 //  * Softmax in base 2 with log2(e) folded into the scale; the running maximum is shared by the 4 lane
-//    groups of a query (two lane swaps per tile); the normaliser is summed once at the end.
+//    groups of a query (two lane swaps per tile).  The normaliser is accumulated on the matrix cores as one
+//    more block of V^T whose first row is ones, which takes its sum off the vector units.
 //  * Only tiles that cross the causal diagonal or the end of the keys are masked.  Work-groups are
 //    launched heaviest query tile first so the long causal rows do not form the tail.
 #include <math.h>
@@ -99,11 +100,15 @@ struct PrefillKernelArgs {
 struct TileSource {
   const uint16_t* kbase;  // this thread's chunk of kv head `kvh` at slot/row 0
   const uint16_t* vbase;
+  const uint16_t* khead;  // kv head `kvh` at slot/row 0 (uniform)
+  const uint16_t* vhead;
   const int32_t* bt_row;  // null: contiguous rows
   int krow;
   int Lk;
   int64_t k_start;
   int64_t slot_elems;
+  bool fast;              // full tiles can use the uniform-base path below
+  int32_t koff[4], voff[4];  // this thread's element offsets inside a tile (rows krow + 16 i, its chunk)
 };
 
 struct Staged {
@@ -117,6 +122,28 @@ __device__ __forceinline__ int block_of(const PrefillKernelArgs& p, const int32_
 
 __device__ __forceinline__ Staged load_tile(const PrefillKernelArgs& p, const TileSource& s, int kt) {
   Staged r;
+  const bool full = (kt + 1) * BN <= s.Lk;
+  if (full && s.fast) {
+    // The tile's 64 rows are consecutive (contiguous mode) or lie in one block: one uniform base per tile and
+    // 32-bit per-thread offsets.
+    const uint16_t *kt_base, *vt_base;
+    if (s.bt_row) {
+      const int key0 = kt * BN;
+      const int64_t slot0 = int64_t(block_of(p, s.bt_row, key0 >> p.bs_shift)) * p.bs + (key0 & (p.bs - 1));
+      kt_base = s.khead + slot0 * s.slot_elems;
+      vt_base = s.vhead + slot0 * s.slot_elems;
+    } else {
+      const int64_t row0 = s.k_start + int64_t(kt) * BN;
+      kt_base = s.khead + row0 * p.k_stride;
+      vt_base = s.vhead + row0 * p.v_stride;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.k[i] = *reinterpret_cast<const u32x4*>(kt_base + s.koff[i]);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vt_base + s.voff[i]);
+    }
+    return r;
+  }
   if (s.bt_row) {
     const bool tile_in_block = p.bs_shift >= 6;
     const int ublk = tile_in_block ? block_of(p, s.bt_row, (kt * BN) >> p.bs_shift) : 0;
@@ -210,17 +237,38 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
   src.Lk = Lk;
   src.k_start = k_start;
   src.slot_elems = int64_t(p.num_kv_heads) * HD;
+  src.khead = p.k + int64_t(kvh) * HD;
+  src.vhead = p.v + int64_t(kvh) * HD;
+  {
+    // Uniform-base path: contiguous rows inside the k rows array, or block_size a multiple of 64; offsets of
+    // a 64-row tile must fit 32 bits.
+    const int64_t ks = p.bt ? src.slot_elems : p.k_stride, vs = p.bt ? src.slot_elems : p.v_stride;
+    src.fast = (!p.bt || p.bs_shift >= 6) && (BN + 1) * max(ks, vs) < (int64_t(1) << 30) &&
+               (p.bt || (k_start >= 0 && k_start + Lk <= p.num_k_rows));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      src.koff[i] = int32_t((src.krow + 16 * i) * ks + (tid & 15) * 8);
+      src.voff[i] = int32_t((src.krow + 16 * i) * vs + (tid & 15) * 8);
+    }
+  }
   Staged st;
 
-  f32x4_t o[8][G];
-  float m[G], l[G];
+  // o_l accumulates the normaliser l = sum of P on the matrix cores, as an extra block of V^T whose first row
+  // is all ones: lane (col, grp 0) ends up holding l of query `col` in o_l[n][0].  It is the sum of the same
+  // bf16-rounded P that multiplies V, rescaled together with O.
+  f32x4_t o[8][G], o_l[G];
+  float m[G];
 #pragma unroll
   for (int n = 0; n < G; ++n) {
     m[n] = kMinusBig;
-    l[n] = 0.f;
+    o_l[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[d][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const uint32_t one2 = col == 0 ? 0x3F803F80u : 0u;  // bf16 pair (1, 1) in row 0 of the block, zeros elsewhere
+  const u32x4 ones = u32x4{one2, one2, one2, one2};
+  // Keys a lane may see: kp <= lim (causal: the query's position; always: the last key).
+  const int lim = p.causal ? min(qpos, Lk - 1) : Lk - 1;
 
   if (n_tiles > 0) {
     st = load_tile(p, src, 0);
@@ -251,6 +299,17 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
     // Mask, online softmax.  Lane holds raw scores of keys kt*64 + 16 kb + 4 grp + r for query `tok`; the
     // scale c > 0 is applied inside exp2(s c - m) (q carries the sign of the scale), m is in scaled units.
     const bool need_mask = (kt + 1) * BN > Lk || (p.causal && (kt + 1) * BN - 1 > qpos0);
+    if (need_mask) {
+      const int room = lim - (kt * BN + grp * 4);  // key kt*64 + 4 grp + 16 kb + r is visible iff 16 kb + r <= room
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool vis = kb * 16 + r <= room;
+#pragma unroll
+          for (int n = 0; n < G; ++n) s[kb][n][r] = vis ? s[kb][n][r] : -INFINITY;
+        }
+    }
     u32x4 pb[G][2];
     bool grew = false;
     float alpha[G];
@@ -260,31 +319,17 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = s[kb][n][r];
-          if (need_mask) {
-            const int kp = kt * BN + kb * 16 + grp * 4 + r;
-            const bool vis = kp < Lk && (!p.causal || kp <= qpos);
-            x = vis ? x : -INFINITY;
-            s[kb][n][r] = x;
-          }
-          mx = fmaxf(mx, x);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][n][r]);
       mx = max_xor32(max_xor16(mx));
       const float mn = fmaxf(m[n], mx * c);
       alpha[n] = fast_exp2(m[n] - mn);
       grew |= mn > m[n];
       m[n] = mn;
-      float sum = 0.f;
       float pv[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pv[kb][r] = fast_exp2(fmaf(s[kb][n][r], c, -mn));
-          sum += pv[kb][r];
-        }
-      l[n] = fmaf(l[n], alpha[n], sum);
+        for (int r = 0; r < 4; ++r) pv[kb][r] = fast_exp2(fmaf(s[kb][n][r], c, -mn));
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         pb[n][h].x = pack_bf16x2(pv[2 * h][0], pv[2 * h][1]);
@@ -296,9 +341,11 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
     // Rescale the output only when some running maximum of the wave moved (rare after the first tiles).
     if (__any(grew)) {
 #pragma unroll
-      for (int n = 0; n < G; ++n)
+      for (int n = 0; n < G; ++n) {
+        o_l[n] *= alpha[n];
 #pragma unroll
         for (int d = 0; d < 8; ++d) o[d][n] *= alpha[n];
+      }
     }
 
     // O^T += V^T P^T.  A operand = V^T: lane (col, grp) needs V[key][16 d + col] for the keys of its P^T slots,
@@ -317,6 +364,8 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
 #pragma unroll
         for (int n = 0; n < G; ++n) o[d][n] = mfma_16x16x32(a, pb[n][h], o[d][n]);
       }
+#pragma unroll
+      for (int n = 0; n < G; ++n) o_l[n] = mfma_16x16x32(ones, pb[n][h], o_l[n]);
     }
 
     if (kt + 1 < n_tiles) store_tile(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
@@ -327,9 +376,7 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
   float inv[G];
 #pragma unroll
   for (int n = 0; n < G; ++n) {
-    float lt = l[n];
-    lt += shfl_xor_f32(lt, 16);
-    lt += shfl_xor_f32(lt, 32);
+    const float lt = __int_as_float(__builtin_amdgcn_ds_bpermute(col << 2, __float_as_int(o_l[n][0])));
     inv[n] = lt > 0.f ? 1.f / lt : 0.f;
   }
   if (tok < Lq && q_start + tok < p.num_q_tokens) {
