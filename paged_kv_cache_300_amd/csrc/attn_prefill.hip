@@ -34,13 +34,16 @@ namespace {
 constexpr int HD = 128;
 constexpr int BM = 64;        // query tokens per work-group
 constexpr int BN = 64;        // keys per tile
-constexpr int THREADS = 256;  // 4 waves x 16 tokens
-// LDS row pitches (elements).  K rows are read 16 rows x 16 B per quarter-wave: a pitch of 272 B puts the
-// 16 reads on distinct banks.  V rows are read 4 rows x 32 B per quarter-wave by the transposing read: a
-// pitch of 288 B (32 B apart modulo 256 B) does the same for them.
-constexpr int KROW = HD + 8;
+constexpr int TOKEN_WAVES = 4; // waves per head slice: 4 x 16 query tokens
+// LDS row pitch (elements) of the K and V tiles: 288 B, i.e. rows 32 B apart modulo 256 B.  With it both
+// the 16-row x 16 B reads of K and the 4-row x 32 B transposing reads of V are free of bank conflicts
+// (measured: SQ_LDS_BANK_CONFLICT = 0; pitches of 256, 272 and 304 B all conflict).
+constexpr int KROW = HD + 16;
 constexpr int VROW = HD + 16;
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef PKV_PREFILL_H2
+#define PKV_PREFILL_H2 2  // query heads per wave for GQA groups of 2
+#endif
 constexpr float kMinusBig = -1e30f;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -111,8 +114,9 @@ struct TileSource {
   int32_t koff[4], voff[4];  // this thread's element offsets inside a tile (rows krow + 16 i, its chunk)
 };
 
+template <int CH>
 struct Staged {
-  u32x4 k[4], v[4];
+  u32x4 k[CH], v[CH];
 };
 
 __device__ __forceinline__ int block_of(const PrefillKernelArgs& p, const int32_t* bt_row, int lb) {
@@ -120,8 +124,11 @@ __device__ __forceinline__ int block_of(const PrefillKernelArgs& p, const int32_
   return (blk >= 0 && blk < p.num_blocks) ? blk : 0;
 }
 
-__device__ __forceinline__ Staged load_tile(const PrefillKernelArgs& p, const TileSource& s, int kt) {
-  Staged r;
+// Thread t of NT moves the 16-byte chunk t % 16 of tile rows krow + (NT / 16) i, i < CH = 1024 / NT.
+template <int CH>
+__device__ __forceinline__ Staged<CH> load_tile(const PrefillKernelArgs& p, const TileSource& s, int kt) {
+  constexpr int RSTEP = 64 / CH;
+  Staged<CH> r;
   const bool full = (kt + 1) * BN <= s.Lk;
   if (full && s.fast) {
     // The tile's 64 rows are consecutive (contiguous mode) or lie in one block: one uniform base per tile and
@@ -138,7 +145,7 @@ __device__ __forceinline__ Staged load_tile(const PrefillKernelArgs& p, const Ti
       vt_base = s.vhead + row0 * p.v_stride;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CH; ++i) {
       r.k[i] = *reinterpret_cast<const u32x4*>(kt_base + s.koff[i]);
       r.v[i] = *reinterpret_cast<const u32x4*>(vt_base + s.voff[i]);
     }
@@ -148,8 +155,8 @@ __device__ __forceinline__ Staged load_tile(const PrefillKernelArgs& p, const Ti
     const bool tile_in_block = p.bs_shift >= 6;
     const int ublk = tile_in_block ? block_of(p, s.bt_row, (kt * BN) >> p.bs_shift) : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(kt * BN + s.krow + 16 * i, s.Lk - 1);
+    for (int i = 0; i < CH; ++i) {
+      const int key = min(kt * BN + s.krow + RSTEP * i, s.Lk - 1);
       int64_t slot;
       if (tile_in_block) {
         slot = int64_t(ublk) * p.bs + (key & (p.bs - 1));
@@ -164,8 +171,8 @@ __device__ __forceinline__ Staged load_tile(const PrefillKernelArgs& p, const Ti
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = min(kt * BN + s.krow + 16 * i, s.Lk - 1);
+    for (int i = 0; i < CH; ++i) {
+      const int key = min(kt * BN + s.krow + RSTEP * i, s.Lk - 1);
       const int64_t row = min(max(s.k_start + key, int64_t(0)), p.num_k_rows - 1);
       r.k[i] = *reinterpret_cast<const u32x4*>(s.kbase + row * p.k_stride);
       r.v[i] = *reinterpret_cast<const u32x4*>(s.vbase + row * p.v_stride);
@@ -174,17 +181,22 @@ __device__ __forceinline__ Staged load_tile(const PrefillKernelArgs& p, const Ti
   return r;
 }
 
-__device__ __forceinline__ void store_tile(const Staged& st, uint16_t* lk, uint16_t* lv, int tid) {
+template <int CH>
+__device__ __forceinline__ void store_tile(const Staged<CH>& st, uint16_t* lk, uint16_t* lv, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
+  for (int i = 0; i < CH; ++i) {
+    const int row = (tid >> 4) + (64 / CH) * i;
     *reinterpret_cast<u32x4*>(&lk[row * KROW + (tid & 15) * 8]) = st.k[i];
     *reinterpret_cast<u32x4*>(&lv[row * VROW + (tid & 15) * 8]) = st.v[i];
   }
 }
 
-template <int G>
-__global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p) {
+// G: query heads per kv head; H: query heads per wave (H divides G).  The work-group has 4 x G / H waves:
+// wave w takes query tokens 16 (w % 4) .. +16 and heads (w / 4) H .. +H of the group.
+template <int G, int H>
+__global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(PrefillKernelArgs p) {
+  constexpr int NT = 64 * TOKEN_WAVES * (G / H);
+  constexpr int CH = 1024 / NT;
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int tile = p.max_tiles - 1 - int(blockIdx.z);  // heaviest (latest) query tiles are dispatched first
   const int q_start = p.cu_q[b];
@@ -204,19 +216,20 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int tok = t0 + wave * 16 + col;  // this lane's query token (column of every MFMA block)
+  const int tok = t0 + (wave % TOKEN_WAVES) * 16 + col;  // this lane's query token (column of every MFMA block)
+  const int hb = (wave / TOKEN_WAVES) * H;                  // first head of the group this wave serves
   const int qpos = Lk - Lq + tok;
 
   // Q^T operands: head n of the group, dims 32*ks + 8*grp .. +8.  A negative scale is carried by q's sign
   // bits (exact in bf16), so the scale applied to the scores is c = |scale| * log2(e).
   const float c = fabsf(p.scale_log2);
   const uint32_t sign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-  u32x4 qreg[G][4];
+  u32x4 qreg[H][4];
   {
     const bool ok = tok < Lq && q_start + tok < p.num_q_tokens;
-    const uint16_t* qrow = p.q + int64_t(q_start + tok) * p.q_stride + int64_t(kvh) * G * HD + grp * 8;
+    const uint16_t* qrow = p.q + int64_t(q_start + tok) * p.q_stride + (int64_t(kvh) * G + hb) * HD + grp * 8;
 #pragma unroll
-    for (int n = 0; n < G; ++n)
+    for (int n = 0; n < H; ++n)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qrow + n * HD + ks * 32) : u32x4{0u, 0u, 0u, 0u};
@@ -246,20 +259,20 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
     src.fast = (!p.bt || p.bs_shift >= 6) && (BN + 1) * max(ks, vs) < (int64_t(1) << 30) &&
                (p.bt || (k_start >= 0 && k_start + Lk <= p.num_k_rows));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      src.koff[i] = int32_t((src.krow + 16 * i) * ks + (tid & 15) * 8);
-      src.voff[i] = int32_t((src.krow + 16 * i) * vs + (tid & 15) * 8);
+    for (int i = 0; i < CH; ++i) {
+      src.koff[i] = int32_t((src.krow + (64 / CH) * i) * ks + (tid & 15) * 8);
+      src.voff[i] = int32_t((src.krow + (64 / CH) * i) * vs + (tid & 15) * 8);
     }
   }
-  Staged st;
+  Staged<CH> st;
 
   // o_l accumulates the normaliser l = sum of P on the matrix cores, as an extra block of V^T whose first row
   // is all ones: lane (col, grp 0) ends up holding l of query `col` in o_l[n][0].  It is the sum of the same
   // bf16-rounded P that multiplies V, rescaled together with O.
-  f32x4_t o[8][G], o_l[G];
-  float m[G];
+  f32x4_t o[8][H], o_l[H];
+  float m[H];
 #pragma unroll
-  for (int n = 0; n < G; ++n) {
+  for (int n = 0; n < H; ++n) {
     m[n] = kMinusBig;
     o_l[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -271,28 +284,28 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
   const int lim = p.causal ? min(qpos, Lk - 1) : Lk - 1;
 
   if (n_tiles > 0) {
-    st = load_tile(p, src, 0);
+    st = load_tile<CH>(p, src, 0);
     store_tile(st, lds_k[0], lds_v[0], tid);
   }
   __syncthreads();
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_tiles) st = load_tile(p, src, kt + 1);
+    if (kt + 1 < n_tiles) st = load_tile<CH>(p, src, kt + 1);
 
     // S^T = K Q^T for 4 blocks of 16 keys.
-    f32x4_t s[4][G];
+    f32x4_t s[4][H];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int n = 0; n < G; ++n) s[kb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < H; ++n) s[kb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&lds_k[buf][(kb * 16 + col) * KROW + ks * 32 + grp * 8]);
 #pragma unroll
-        for (int n = 0; n < G; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
+        for (int n = 0; n < H; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
       }
     }
 
@@ -307,14 +320,14 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
         for (int r = 0; r < 4; ++r) {
           const bool vis = kb * 16 + r <= room;
 #pragma unroll
-          for (int n = 0; n < G; ++n) s[kb][n][r] = vis ? s[kb][n][r] : -INFINITY;
+          for (int n = 0; n < H; ++n) s[kb][n][r] = vis ? s[kb][n][r] : -INFINITY;
         }
     }
-    u32x4 pb[G][2];
+    u32x4 pb[H][2];
     bool grew = false;
-    float alpha[G];
+    float alpha[H];
 #pragma unroll
-    for (int n = 0; n < G; ++n) {
+    for (int n = 0; n < H; ++n) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -341,7 +354,7 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
     // Rescale the output only when some running maximum of the wave moved (rare after the first tiles).
     if (__any(grew)) {
 #pragma unroll
-      for (int n = 0; n < G; ++n) {
+      for (int n = 0; n < H; ++n) {
         o_l[n] *= alpha[n];
 #pragma unroll
         for (int d = 0; d < 8; ++d) o[d][n] *= alpha[n];
@@ -362,10 +375,10 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
         const u32x2 hi = ds_read_tr16(vrow + 16 * VROW + d * 16);
         const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int n = 0; n < G; ++n) o[d][n] = mfma_16x16x32(a, pb[n][h], o[d][n]);
+        for (int n = 0; n < H; ++n) o[d][n] = mfma_16x16x32(a, pb[n][h], o[d][n]);
       }
 #pragma unroll
-      for (int n = 0; n < G; ++n) o_l[n] = mfma_16x16x32(ones, pb[n][h], o_l[n]);
+      for (int n = 0; n < H; ++n) o_l[n] = mfma_16x16x32(ones, pb[n][h], o_l[n]);
     }
 
     if (kt + 1 < n_tiles) store_tile(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
@@ -373,16 +386,16 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
   }
 
   // Normalise and write: lane holds dims 16 d + 4 grp + r of query `tok`, head kvh*G + n.
-  float inv[G];
+  float inv[H];
 #pragma unroll
-  for (int n = 0; n < G; ++n) {
+  for (int n = 0; n < H; ++n) {
     const float lt = __int_as_float(__builtin_amdgcn_ds_bpermute(col << 2, __float_as_int(o_l[n][0])));
     inv[n] = lt > 0.f ? 1.f / lt : 0.f;
   }
   if (tok < Lq && q_start + tok < p.num_q_tokens) {
 #pragma unroll
-    for (int n = 0; n < G; ++n) {
-      uint16_t* orow = p.out + (int64_t(q_start + tok) * p.num_q_heads + kvh * G + n) * HD + grp * 4;
+    for (int n = 0; n < H; ++n) {
+      uint16_t* orow = p.out + (int64_t(q_start + tok) * p.num_q_heads + kvh * G + hb + n) * HD + grp * 4;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         u32x2 w;
@@ -394,16 +407,17 @@ __global__ void __launch_bounds__(THREADS, 2) prefill_kernel(PrefillKernelArgs p
   }
 }
 
-template <int G>
+template <int G, int H>
 hipError_t launch_g(const PrefillKernelArgs& p, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_kernel<G>, dim3(p.num_kv_heads, batch, p.max_tiles), dim3(THREADS), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<G, H>), dim3(p.num_kv_heads, batch, p.max_tiles), dim3(64 * TOKEN_WAVES * (G / H)), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool prefill_fast_supported(int head_dim, int group, bool bf16) {
-  return bf16 && head_dim == HD && (group == 1 || group == 2);
+  return bf16 && head_dim == HD && (group == 1 || group == 2 || group == 4);
 }
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
@@ -431,7 +445,9 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
   p.out = static_cast<uint16_t*>(a.out);
   if (p.max_tiles > 65535) return hipErrorInvalidConfiguration;
   const int group = a.num_q_heads / a.num_kv_heads;
-  return group == 1 ? launch_g<1>(p, a.batch, stream) : launch_g<2>(p, a.batch, stream);
+  return group == 1   ? launch_g<1, 1>(p, a.batch, stream)
+         : group == 2 ? launch_g<2, PKV_PREFILL_H2>(p, a.batch, stream)
+                      : launch_g<4, 2>(p, a.batch, stream);
 }
 
 }  // namespace pkv
