@@ -54,7 +54,7 @@ enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = -1, /* a null pointer, a negative size, inconsistent shapes or strides */
   PKV_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement (e.g. head_dim > 256) */
-  PKV_ERR_WORKSPACE = -3,   /* attn_decode_paged: workspace missing or smaller than required */
+  PKV_ERR_WORKSPACE = -3,   /* a workspace smaller than its size function requires (or missing for decode) */
   PKV_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
 };
 
@@ -108,16 +108,30 @@ int kv_store(const void* key, int64_t key_stride, const void* value, int64_t val
  * out: [num_q_tokens, num_q_heads, head_dim], contiguous, same dtype as q.
  * max_seqlen_q must be >= every Lq (rows beyond it are not computed); max_seqlen_k is accepted for
  *   signature parity with the pages' call and only checked to be >= 0.
+ * workspace: NULL, or device memory of at least attn_prefill_workspace_bytes(...) bytes (contents on
+ *   entry do not matter).  With it the bf16 head_dim-128 kernel runs a one-work-group planner that lists
+ *   the query tiles longest first, so that the rows with the most keys (long cached prefixes, non-causal
+ *   rows) start first and short ones fill the tail; without it the tiles are launched latest-first, which
+ *   is the same order for causal attention over a step's own tokens (there the workspace is not used).
+ *   Results do not depend on the order.
  * Unspecified (but in-bounds) results: query rows past num_q_tokens are skipped; key rows past
- *   num_k_rows and block-table entries outside [0, num_blocks) are treated as masked.
+ *   num_k_rows and block-table entries outside [0, num_blocks) give unspecified values without any
+ *   out-of-bounds access.
  */
 int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t k_stride, const void* v,
                         int64_t v_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                         int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t batch, int32_t num_q_tokens,
                         int64_t num_k_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         float softmax_scale, int32_t causal, const int32_t* block_tables,
-                        int32_t max_blocks_per_seq, int32_t block_size, void* out, pkv_dtype dtype,
-                        hipStream_t stream);
+                        int32_t max_blocks_per_seq, int32_t block_size, void* out, void* workspace,
+                        size_t workspace_bytes, pkv_dtype dtype, hipStream_t stream);
+
+/*
+ * attn_prefill_workspace_bytes -- bytes of device workspace attn_prefill_varlen can use for these sizes
+ * (0: it takes none): a count and one (sequence, query tile) entry per possible query tile.
+ */
+size_t attn_prefill_workspace_bytes(int32_t batch, int32_t num_q_tokens, int32_t max_seqlen_q, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype);
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_paged needs for these sizes

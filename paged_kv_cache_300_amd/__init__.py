@@ -21,6 +21,7 @@ from ._lib import (
     kv_slot_mapping,
     kv_store,
     attn_prefill_varlen,
+    attn_prefill_workspace_bytes,
     attn_decode_workspace_bytes,
     attn_decode_paged,
 )
@@ -34,6 +35,7 @@ __all__ = [
     "kv_slot_mapping",
     "kv_store",
     "attn_prefill_varlen",
+    "attn_prefill_workspace_bytes",
     "attn_decode_workspace_bytes",
     "attn_decode_paged",
 ]

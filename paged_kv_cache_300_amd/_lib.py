@@ -43,8 +43,10 @@ def lib():
     L.kv_store.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i32, i32, i32, ctypes.c_int, vp]
     L.kv_store.restype = ctypes.c_int
     L.attn_prefill_varlen.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
-                                      f32, i32, vp, i32, i32, vp, ctypes.c_int, vp]
+                                      f32, i32, vp, i32, i32, vp, vp, sz, ctypes.c_int, vp]
     L.attn_prefill_varlen.restype = ctypes.c_int
+    L.attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int]
+    L.attn_prefill_workspace_bytes.restype = sz
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode_paged.argtypes = [vp, i64, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz,
@@ -150,9 +152,20 @@ def kv_store(key, value, k_cache, v_cache, slot_mapping):
     _check("kv_store", rc)
 
 
+def attn_prefill_workspace_bytes(batch, num_q_tokens, max_seqlen_q, num_q_heads, num_kv_heads, head_dim,
+                                 dtype=torch.bfloat16):
+    code = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
+    return int(lib().attn_prefill_workspace_bytes(batch, num_q_tokens, max_seqlen_q, num_q_heads, num_kv_heads,
+                                                  head_dim, code))
+
+
 def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale,
-                        causal=True, block_table=None, out=None):
-    """Varlen (causal) attention; with ``block_table`` the keys come from the paged caches ``k``, ``v``."""
+                        causal=True, block_table=None, out=None, order=True, workspace=None):
+    """Varlen (causal) attention; with ``block_table`` the keys come from the paged caches ``k``, ``v``.
+
+    ``order``: let the library list the query tiles longest first (bf16, head_dim 128) in ``workspace``
+    (uint8 device tensor of ``attn_prefill_workspace_bytes`` bytes; allocated here when not given).
+    """
     _dev(q, "q")
     _meta(cu_seqlens_q, "cu_seqlens_q"); _meta(cu_seqlens_k, "cu_seqlens_k"); _meta(block_table, "block_table")
     nq, hq, hd = q.shape
@@ -183,10 +196,19 @@ def attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_s
         out = torch.empty((nq, hq, hd), dtype=q.dtype, device=q.device)
     elif out.shape != (nq, hq, hd) or not out.is_contiguous() or out.dtype != q.dtype:
         raise ValueError("out must be a contiguous [Nq, Hq, head_dim] tensor of q's dtype")
+    ws_bytes = 0
+    if not order:
+        workspace = None
+    elif workspace is None and batch > 0:
+        need = attn_prefill_workspace_bytes(batch, nq, int(max_seqlen_q), hq, hkv, hd, q.dtype)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().attn_prefill_varlen(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                    int(max_seqlen_q), int(max_seqlen_k), batch, nq, num_k_rows, hq, hkv, hd,
                                    float(softmax_scale), 1 if causal else 0, _ptr(block_table), max_blocks, bs,
-                                   _ptr(out), _dtype_code(q), _stream(q))
+                                   _ptr(out), _ptr(workspace), ws_bytes, _dtype_code(q), _stream(q))
     _check("attn_prefill_varlen", rc)
     return out
 

@@ -103,8 +103,8 @@ int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t 
                         int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t batch, int32_t num_q_tokens,
                         int64_t num_k_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         float softmax_scale, int32_t causal, const int32_t* block_tables,
-                        int32_t max_blocks_per_seq, int32_t block_size, void* out, pkv_dtype dtype,
-                        hipStream_t stream) {
+                        int32_t max_blocks_per_seq, int32_t block_size, void* out, void* workspace,
+                        size_t workspace_bytes, pkv_dtype dtype, hipStream_t stream) {
   g_error.clear();
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
@@ -145,10 +145,27 @@ int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t 
   const bool bf16 = dtype == PKV_BF16;
   const bool fast = pkv::prefill_fast_supported(head_dim, num_q_heads / num_kv_heads, bf16) && aligned16(q) &&
                     aligned16(k) && aligned16(v) && aligned16(out) && q_stride % 8 == 0 &&
-                    k_stride % 8 == 0 && v_stride % 8 == 0;
-  if (fast)
-    return hip_status(pkv::launch_prefill_bf16(a, stream), "attn_prefill_varlen launch");
+                    k_stride % 8 == 0 && v_stride % 8 == 0 && pkv::prefill_fast_strides_ok(k_stride, v_stride);
+  if (fast) {
+    if (workspace) {
+      const size_t need = pkv::prefill_workspace_bytes(batch, num_q_tokens, max_seqlen_q, num_kv_heads);
+      if (need > 0 && workspace_bytes < need)
+        return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+      if (need == 0 || !pkv::prefill_wants_order(a, max_seqlen_k)) workspace = nullptr;
+    }
+    return hip_status(pkv::launch_prefill_bf16(a, workspace, workspace_bytes, stream),
+                      "attn_prefill_varlen launch");
+  }
   return hip_status(pkv::launch_attn_generic(a, bf16, stream), "attn_prefill_varlen launch");
+}
+
+size_t attn_prefill_workspace_bytes(int32_t batch, int32_t num_q_tokens, int32_t max_seqlen_q, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype) {
+  if (batch <= 0 || num_q_tokens < 0 || max_seqlen_q < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads || dtype != PKV_BF16)
+    return 0;
+  if (!pkv::prefill_fast_supported(head_dim, num_q_heads / num_kv_heads, true)) return 0;
+  return pkv::prefill_workspace_bytes(batch, num_q_tokens, max_seqlen_q, num_kv_heads);
 }
 
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

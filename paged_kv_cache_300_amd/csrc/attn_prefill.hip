@@ -25,6 +25,8 @@
 //    launched heaviest query tile first so the long causal rows do not form the tail.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -45,6 +47,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 #define PKV_PREFILL_H2 2  // query heads per wave for GQA groups of 2
 #endif
 constexpr float kMinusBig = -1e30f;
+constexpr float kRescaleSlack = 8.f;  // log2 units: weights up to 2^8 before the output is rescaled
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
@@ -100,18 +103,31 @@ struct PrefillKernelArgs {
   uint16_t* out;
 };
 
+// How K/V tiles reach LDS.  CONTIG: rows of this step's k/v arrays; PAGED: the paged cache with a block size
+// that is a power of two >= 64, so a 64-key tile lies inside one block.  Both read a tile as one buffer
+// resource (base = the tile's first row, size = its valid rows), so rows past the end of the sequence come
+// back as zeros without any per-lane check.  ROWS: any other block size, one block-table lookup per row.
+enum : int { LOAD_CONTIG = 0, LOAD_PAGED = 1, LOAD_ROWS = 2 };
+
+// Raw buffer: stride 0, 32-bit data format; an offset at or past num_records reads 0 and touches no memory.
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, int(bytes), kBufferFlags);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 struct TileSource {
-  const uint16_t* kbase;  // this thread's chunk of kv head `kvh` at slot/row 0
-  const uint16_t* vbase;
-  const uint16_t* khead;  // kv head `kvh` at slot/row 0 (uniform)
+  const uint16_t* khead;  // kv head `kvh` at row / slot 0
   const uint16_t* vhead;
-  const int32_t* bt_row;  // null: contiguous rows
-  int krow;
+  const int32_t* bt_row;  // PAGED / ROWS: this sequence's block-table row
+  int krow;               // first tile row this thread moves
   int Lk;
-  int64_t k_start;
-  int64_t slot_elems;
-  bool fast;              // full tiles can use the uniform-base path below
-  int32_t koff[4], voff[4];  // this thread's element offsets inside a tile (rows krow + 16 i, its chunk)
+  int64_t k_start;        // CONTIG: first row of the sequence
+  int64_t kstride, vstride;  // elements between consecutive rows (CONTIG) or slots (PAGED / ROWS)
+  uint32_t koff[4], voff[4];  // CONTIG / PAGED: byte offsets of this thread's chunks inside a tile
 };
 
 template <int CH>
@@ -125,57 +141,43 @@ __device__ __forceinline__ int block_of(const PrefillKernelArgs& p, const int32_
 }
 
 // Thread t of NT moves the 16-byte chunk t % 16 of tile rows krow + (NT / 16) i, i < CH = 1024 / NT.
-template <int CH>
-__device__ __forceinline__ Staged<CH> load_tile(const PrefillKernelArgs& p, const TileSource& s, int kt) {
+// `blk` is the cache block holding tile kt (PAGED only).
+template <int MODE, int CH>
+__device__ __forceinline__ Staged<CH> load_tile(const PrefillKernelArgs& p, const TileSource& s, int kt, int blk) {
   constexpr int RSTEP = 64 / CH;
   Staged<CH> r;
-  const bool full = (kt + 1) * BN <= s.Lk;
-  if (full && s.fast) {
-    // The tile's 64 rows are consecutive (contiguous mode) or lie in one block: one uniform base per tile and
-    // 32-bit per-thread offsets.
-    const uint16_t *kt_base, *vt_base;
-    if (s.bt_row) {
-      const int key0 = kt * BN;
-      const int64_t slot0 = int64_t(block_of(p, s.bt_row, key0 >> p.bs_shift)) * p.bs + (key0 & (p.bs - 1));
-      kt_base = s.khead + slot0 * s.slot_elems;
-      vt_base = s.vhead + slot0 * s.slot_elems;
+  if constexpr (MODE == LOAD_CONTIG || MODE == LOAD_PAGED) {
+    int rows = min(s.Lk - kt * BN, BN);
+    const uint16_t *kb, *vb;
+    if constexpr (MODE == LOAD_PAGED) {
+      blk = __builtin_amdgcn_readfirstlane(blk);  // uniform by construction; keeps the tile base in SGPRs
+      const int64_t slot0 = int64_t(blk) * p.bs + ((kt * BN) & (p.bs - 1));
+      kb = s.khead + slot0 * s.kstride;
+      vb = s.vhead + slot0 * s.vstride;
     } else {
       const int64_t row0 = s.k_start + int64_t(kt) * BN;
-      kt_base = s.khead + row0 * p.k_stride;
-      vt_base = s.vhead + row0 * p.v_stride;
+      rows = row0 < 0 ? 0 : int(min(int64_t(rows), p.num_k_rows - row0));
+      kb = s.khead + row0 * s.kstride;
+      vb = s.vhead + row0 * s.vstride;
     }
+    rows = __builtin_amdgcn_readfirstlane(max(rows, 0));  // uniform; keeps the resource in SGPRs
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, uint32_t(rows) * uint32_t(s.kstride) * 2u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, uint32_t(rows) * uint32_t(s.vstride) * 2u);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      r.k[i] = *reinterpret_cast<const u32x4*>(kt_base + s.koff[i]);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vt_base + s.voff[i]);
-    }
-    return r;
-  }
-  if (s.bt_row) {
-    const bool tile_in_block = p.bs_shift >= 6;
-    const int ublk = tile_in_block ? block_of(p, s.bt_row, (kt * BN) >> p.bs_shift) : 0;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int key = min(kt * BN + s.krow + RSTEP * i, s.Lk - 1);
-      int64_t slot;
-      if (tile_in_block) {
-        slot = int64_t(ublk) * p.bs + (key & (p.bs - 1));
-      } else if (p.bs_shift >= 0) {
-        slot = int64_t(block_of(p, s.bt_row, key >> p.bs_shift)) * p.bs + (key & (p.bs - 1));
-      } else {
-        const int lb = key / p.bs;
-        slot = int64_t(block_of(p, s.bt_row, lb)) * p.bs + (key - lb * p.bs);
-      }
-      r.k[i] = *reinterpret_cast<const u32x4*>(s.kbase + slot * s.slot_elems);
-      r.v[i] = *reinterpret_cast<const u32x4*>(s.vbase + slot * s.slot_elems);
+      r.k[i] = buffer_load16(rk, s.koff[i]);
+      r.v[i] = buffer_load16(rv, s.voff[i]);
     }
   } else {
+    // Keys past the end of the sequence read its last key (finite; masked, weight exactly 0).  Lk >= 1 here.
+    const int chunk = (threadIdx.x & 15) * 8;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int key = min(kt * BN + s.krow + RSTEP * i, s.Lk - 1);
-      const int64_t row = min(max(s.k_start + key, int64_t(0)), p.num_k_rows - 1);
-      r.k[i] = *reinterpret_cast<const u32x4*>(s.kbase + row * p.k_stride);
-      r.v[i] = *reinterpret_cast<const u32x4*>(s.vbase + row * p.v_stride);
+      const int lb = key / p.bs;
+      const int64_t slot = int64_t(block_of(p, s.bt_row, lb)) * p.bs + (key - lb * p.bs);
+      r.k[i] = *reinterpret_cast<const u32x4*>(s.khead + slot * s.kstride + chunk);
+      r.v[i] = *reinterpret_cast<const u32x4*>(s.vhead + slot * s.vstride + chunk);
     }
   }
   return r;
@@ -191,28 +193,49 @@ __device__ __forceinline__ void store_tile(const Staged<CH>& st, uint16_t* lk, u
   }
 }
 
-// G: query heads per kv head; H: query heads per wave (H divides G).  The work-group has 4 x G / H waves:
-// wave w takes query tokens 16 (w % 4) .. +16 and heads (w / 4) H .. +H of the group.
-template <int G, int H>
-__global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(PrefillKernelArgs p) {
-  constexpr int NT = 64 * TOKEN_WAVES * (G / H);
-  constexpr int CH = 1024 / NT;
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int tile = p.max_tiles - 1 - int(blockIdx.z);  // heaviest (latest) query tiles are dispatched first
-  const int q_start = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - q_start;
-  if (tile * BM >= Lq) return;
-  const int64_t k_start = p.cu_k[b];
+// Per-sequence geometry of the work decomposition.
+struct SeqGeom {
+  int q_start;      // first query row of the sequence
+  int Lq, Lk;       // new tokens; visible keys (paged mode: clamped to the block table)
+  int64_t k_start;  // contiguous mode: first key row
+  int T;            // query tiles
+  int NKe;          // key tiles of an unmasked row, at least 1
+  int c0;           // query tile t attends key tiles [0, clamp(t + 1 + c0, 1, NKe))
+};
+
+__device__ __forceinline__ int ceil_div64(int x) { return x >= 0 ? (x + 63) >> 6 : -((-x) >> 6); }
+
+__device__ __forceinline__ SeqGeom seq_geom(const PrefillKernelArgs& p, int b) {
+  SeqGeom g;
+  g.q_start = p.cu_q[b];
+  g.Lq = max(p.cu_q[b + 1] - g.q_start, 0);
+  g.k_start = p.cu_k[b];
   int Lk = max(p.cu_k[b + 1] - p.cu_k[b], 0);
   if (p.bt) Lk = min(Lk, p.max_blocks * p.bs);
-  const int t0 = tile * BM;
-  const int qpos0 = Lk - Lq + t0;  // absolute position of the work-group's first query row
-  int kend = p.causal ? min(Lk, qpos0 + BM) : Lk;
-  kend = max(kend, 0);
-  const int n_tiles = (kend + BN - 1) / BN;
+  g.Lk = Lk;
+  g.T = (g.Lq + BM - 1) / BM;
+  g.NKe = max((Lk + BN - 1) / BN, 1);
+  // Causal: the last query of tile t sits at position Lk - Lq + 64 t + 63, so it sees ceil((Lk - Lq)/64) + t + 1
+  // key tiles.  A tile with no visible key still runs one fully masked key tile, which writes zeros.
+  g.c0 = p.causal ? ceil_div64(Lk - g.Lq) : g.NKe;
+  return g;
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * VROW];
+__device__ __forceinline__ int unit_tiles(const SeqGeom& g, int t) { return min(max(t + 1 + g.c0, 1), g.NKe); }
+
+// Flash attention of query tile t of sequence `g` (kv head kvh, its G query heads) against key tiles [kt0, kt1):
+// leaves the unnormalised output o, the normaliser (o_l[n][0] of lanes with grp 0) and the reference maximum m.
+// Ends with a barrier, so the LDS tiles are free on return.
+template <int G, int H, int MODE>
+__device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const SeqGeom& g, int b, int kvh, int t,
+                                             int kt0, int kt1, uint16_t (*lds_k)[BN * KROW],
+                                             uint16_t (*lds_v)[BN * VROW], f32x4_t (&o)[8][H], f32x4_t (&o_l)[H],
+                                             float (&m)[H]) {
+  constexpr int NT = 64 * TOKEN_WAVES * (G / H);
+  constexpr int CH = 1024 / NT;
+  const int Lq = g.Lq, Lk = g.Lk, q_start = g.q_start;
+  const int t0 = t * BM;
+  const int qpos0 = Lk - Lq + t0;  // absolute position of the tile's first query row
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -220,9 +243,22 @@ __global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(
   const int hb = (wave / TOKEN_WAVES) * H;                  // first head of the group this wave serves
   const int qpos = Lk - Lq + tok;
 
+#pragma unroll
+  for (int n = 0; n < H; ++n) {
+    m[n] = kMinusBig;
+    o_l[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // No query of the tile sees a key (no keys, or every query before the first key): the output is zero and
+  // nothing is read.
+  if ((p.causal ? min(Lk, qpos0 + BM) : Lk) <= 0) return;
+
   // Q^T operands: head n of the group, dims 32*ks + 8*grp .. +8.  A negative scale is carried by q's sign
-  // bits (exact in bf16), so the scale applied to the scores is c = |scale| * log2(e).
-  const float c = fabsf(p.scale_log2);
+  // bits (exact in bf16), so the scale applied to the scores is c = |scale| * log2(e) > 0 (a zero scale is
+  // taken as the smallest normal float: every weight is then 1 to within rounding, as it should be, and
+  // masked scores stay -inf).
+  const float c = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
   const uint32_t sign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   u32x4 qreg[H][4];
   {
@@ -238,60 +274,45 @@ __global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(
       }
   }
 
-  // Staging: thread t moves the 16-byte chunk (t % 16) of key rows t / 16 + 16 i (i < 4) of the K and V tiles.
-  // Keys past the end of the sequence read its last key instead (finite data; their scores are masked and
-  // their weights are exactly 0), so the loads need no branches.  In paged mode with block_size a multiple
-  // of 64 a whole tile lies in one block: one uniform block-table read per tile.
+  // Staging: thread t moves the 16-byte chunk (t % 16) of key rows t / 16 + (64 / CH) i of the K and V tiles.
   TileSource src;
-  src.kbase = p.k + int64_t(kvh) * HD + (tid & 15) * 8;
-  src.vbase = p.v + int64_t(kvh) * HD + (tid & 15) * 8;
+  src.khead = p.k + int64_t(kvh) * HD;
+  src.vhead = p.v + int64_t(kvh) * HD;
   src.bt_row = p.bt ? p.bt + int64_t(b) * p.max_blocks : nullptr;
   src.krow = tid >> 4;
   src.Lk = Lk;
-  src.k_start = k_start;
-  src.slot_elems = int64_t(p.num_kv_heads) * HD;
-  src.khead = p.k + int64_t(kvh) * HD;
-  src.vhead = p.v + int64_t(kvh) * HD;
-  {
-    // Uniform-base path: contiguous rows inside the k rows array, or block_size a multiple of 64; offsets of
-    // a 64-row tile must fit 32 bits.
-    const int64_t ks = p.bt ? src.slot_elems : p.k_stride, vs = p.bt ? src.slot_elems : p.v_stride;
-    src.fast = (!p.bt || p.bs_shift >= 6) && (BN + 1) * max(ks, vs) < (int64_t(1) << 30) &&
-               (p.bt || (k_start >= 0 && k_start + Lk <= p.num_k_rows));
+  src.k_start = g.k_start;
+  src.kstride = p.bt ? int64_t(p.num_kv_heads) * HD : p.k_stride;
+  src.vstride = p.bt ? int64_t(p.num_kv_heads) * HD : p.v_stride;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      src.koff[i] = int32_t((src.krow + (64 / CH) * i) * ks + (tid & 15) * 8);
-      src.voff[i] = int32_t((src.krow + (64 / CH) * i) * vs + (tid & 15) * 8);
-    }
+  for (int i = 0; i < CH; ++i) {
+    src.koff[i] = uint32_t(((src.krow + (64 / CH) * i) * src.kstride + (tid & 15) * 8) * 2);
+    src.voff[i] = uint32_t(((src.krow + (64 / CH) * i) * src.vstride + (tid & 15) * 8) * 2);
   }
+  // PAGED: the block of the next tile to load is read one tile ahead, off the critical path.
+  auto tile_block = [&](int kt) { return MODE == LOAD_PAGED ? block_of(p, src.bt_row, (kt * BN) >> p.bs_shift) : 0; };
   Staged<CH> st;
 
   // o_l accumulates the normaliser l = sum of P on the matrix cores, as an extra block of V^T whose first row
   // is all ones: lane (col, grp 0) ends up holding l of query `col` in o_l[n][0].  It is the sum of the same
   // bf16-rounded P that multiplies V, rescaled together with O.
-  f32x4_t o[8][H], o_l[H];
-  float m[H];
-#pragma unroll
-  for (int n = 0; n < H; ++n) {
-    m[n] = kMinusBig;
-    o_l[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
   const uint32_t one2 = col == 0 ? 0x3F803F80u : 0u;  // bf16 pair (1, 1) in row 0 of the block, zeros elsewhere
   const u32x4 ones = u32x4{one2, one2, one2, one2};
   // Keys a lane may see: kp <= lim (causal: the query's position; always: the last key).
   const int lim = p.causal ? min(qpos, Lk - 1) : Lk - 1;
 
-  if (n_tiles > 0) {
-    st = load_tile<CH>(p, src, 0);
-    store_tile(st, lds_k[0], lds_v[0], tid);
-  }
+  int next_blk = 0;
+  st = load_tile<MODE, CH>(p, src, kt0, tile_block(kt0));
+  if (kt0 + 1 < kt1) next_blk = tile_block(kt0 + 1);
+  store_tile(st, lds_k[0], lds_v[0], tid);
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_tiles) st = load_tile<CH>(p, src, kt + 1);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    if (kt + 1 < kt1) {
+      st = load_tile<MODE, CH>(p, src, kt + 1, next_blk);
+      if (kt + 2 < kt1) next_blk = tile_block(kt + 2);
+    }
 
     // S^T = K Q^T for 4 blocks of 16 keys.
     f32x4_t s[4][H];
@@ -323,41 +344,46 @@ __global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(
           for (int n = 0; n < H; ++n) s[kb][n][r] = vis ? s[kb][n][r] : -INFINITY;
         }
     }
-    u32x4 pb[H][2];
-    bool grew = false;
-    float alpha[H];
+    // The reference maximum m only moves when a tile's maximum exceeds it by more than kRescaleSlack (in
+    // log2 units), so the weights exp2(s c - m) stay <= 2^kRescaleSlack and the O / l rescale -- a multiply
+    // of every accumulator -- is rare after the first tile.  Any reference value gives the same O / l.
+    float mxc[H];
+    bool need = false;
 #pragma unroll
     for (int n = 0; n < H; ++n) {
-      float mx = -INFINITY;
+      float mx = s[0][n][0];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][n][r]);
-      mx = max_xor32(max_xor16(mx));
-      const float mn = fmaxf(m[n], mx * c);
-      alpha[n] = fast_exp2(m[n] - mn);
-      grew |= mn > m[n];
-      m[n] = mn;
+        for (int r = (kb == 0 ? 1 : 0); r < 4; ++r) mx = __builtin_elementwise_maximum(mx, s[kb][n][r]);
+      mxc[n] = max_xor32(max_xor16(mx)) * c;
+      need |= mxc[n] > m[n] + kRescaleSlack;
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int n = 0; n < H; ++n) {
+        const float mn = fmaxf(m[n], mxc[n]);
+        const float alpha = fast_exp2(m[n] - mn);
+        m[n] = mn;
+        o_l[n] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[d][n] *= alpha;
+      }
+    }
+    u32x4 pb[H][2];
+#pragma unroll
+    for (int n = 0; n < H; ++n) {
       float pv[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[kb][r] = fast_exp2(fmaf(s[kb][n][r], c, -mn));
+        for (int r = 0; r < 4; ++r) pv[kb][r] = fast_exp2(fmaf(s[kb][n][r], c, -m[n]));
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         pb[n][h].x = pack_bf16x2(pv[2 * h][0], pv[2 * h][1]);
         pb[n][h].y = pack_bf16x2(pv[2 * h][2], pv[2 * h][3]);
         pb[n][h].z = pack_bf16x2(pv[2 * h + 1][0], pv[2 * h + 1][1]);
         pb[n][h].w = pack_bf16x2(pv[2 * h + 1][2], pv[2 * h + 1][3]);
-      }
-    }
-    // Rescale the output only when some running maximum of the wave moved (rare after the first tiles).
-    if (__any(grew)) {
-#pragma unroll
-      for (int n = 0; n < H; ++n) {
-        o_l[n] *= alpha[n];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[d][n] *= alpha[n];
       }
     }
 
@@ -381,21 +407,29 @@ __global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(
       for (int n = 0; n < H; ++n) o_l[n] = mfma_16x16x32(ones, pb[n][h], o_l[n]);
     }
 
-    if (kt + 1 < n_tiles) store_tile(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
+    if (kt + 1 < kt1) store_tile(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
     __syncthreads();
   }
+}
 
-  // Normalise and write: lane holds dims 16 d + 4 grp + r of query `tok`, head kvh*G + n.
+// Normalise and write: lane holds dims 16 d + 4 grp + r of query `tok`, head kvh*G + hb + n.
+template <int G, int H>
+__device__ __forceinline__ void write_output(const PrefillKernelArgs& p, const SeqGeom& g, int kvh, int t,
+                                             const f32x4_t (&o)[8][H], const f32x4_t (&o_l)[H]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int tok = t * BM + (wave % TOKEN_WAVES) * 16 + col;
+  const int hb = (wave / TOKEN_WAVES) * H;
   float inv[H];
 #pragma unroll
   for (int n = 0; n < H; ++n) {
     const float lt = __int_as_float(__builtin_amdgcn_ds_bpermute(col << 2, __float_as_int(o_l[n][0])));
     inv[n] = lt > 0.f ? 1.f / lt : 0.f;
   }
-  if (tok < Lq && q_start + tok < p.num_q_tokens) {
+  if (tok < g.Lq && g.q_start + tok < p.num_q_tokens) {
 #pragma unroll
     for (int n = 0; n < H; ++n) {
-      uint16_t* orow = p.out + (int64_t(q_start + tok) * p.num_q_heads + kvh * G + hb + n) * HD + grp * 4;
+      uint16_t* orow = p.out + (int64_t(g.q_start + tok) * p.num_q_heads + kvh * G + hb + n) * HD + grp * 4;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         u32x2 w;
@@ -407,11 +441,164 @@ __global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(
   }
 }
 
+// G: query heads per kv head; H: query heads per wave (H divides G).  The work-group has 4 x G / H waves:
+// wave w takes query tokens 16 (w % 4) .. +16 and heads (w / 4) H .. +H of the group.
+// Grid form: one work-group per (kv head, sequence, query tile), heaviest (latest) query tiles dispatched first.
+template <int G, int H, int MODE>
+__global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(PrefillKernelArgs p) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int t = p.max_tiles - 1 - int(blockIdx.z);
+  const SeqGeom g = seq_geom(p, b);
+  if (t >= g.T) return;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * VROW];
+  f32x4_t o[8][H], o_l[H];
+  float m[H];
+  attend_tiles<G, H, MODE>(p, g, b, kvh, t, 0, unit_tiles(g, t), lds_k, lds_v, o, o_l, m);
+  write_output<G, H>(p, g, kvh, t, o, o_l);
+}
+
+// Longest-first order.  When the work of a query tile is not given by its index (cached prefixes of different
+// lengths, non-causal rows), a one-work-group planner lists the (sequence, query tile) units by key-tile count,
+// largest first, and the ordered kernel takes unit `rank` = its launch index / Hkv: the hardware hands out work-
+// groups in launch order, so the longest rows start first and the short ones fill the tail (greedy
+// longest-processing-time scheduling, with no communication between work-groups).
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_MAX_BATCH = 4096;
+constexpr int PLAN_BUCKETS = 4096;  // units with more key tiles share the last bucket
+constexpr size_t PLAN_HEADER_BYTES = 256;
+
+struct PlanArgs {
+  int batch;
+  int unit_cap;  // list capacity; units past it are dropped (the host sizes it from num_q_tokens)
+  int2* list;    // [unit_cap] (sequence, query tile), longest first
+  int* count;    // number of listed units
+};
+
+// Exclusive prefix sum of a[0 .. n) in place (n <= 4 * PLAN_THREADS); returns the total.  All threads call it.
+__device__ int block_exclusive_scan(int* a, int n, int* chunk) {
+  const int tid = threadIdx.x;
+  const int per = (n + PLAN_THREADS - 1) / PLAN_THREADS;
+  const int c_beg = min(tid * per, n), c_end = min(c_beg + per, n);
+  int acc = 0;
+  for (int i = c_beg; i < c_end; ++i) acc += a[i];
+  chunk[tid] = acc;
+  __syncthreads();
+  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
+    const int x = tid >= off ? chunk[tid - off] : 0;
+    __syncthreads();
+    chunk[tid] += x;
+    __syncthreads();
+  }
+  const int total = chunk[PLAN_THREADS - 1];
+  acc = tid > 0 ? chunk[tid - 1] : 0;
+  for (int i = c_beg; i < c_end; ++i) {
+    const int x = a[i];
+    a[i] = acc;
+    acc += x;
+  }
+  __syncthreads();
+  return total;
+}
+
+__global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(PrefillKernelArgs p, PlanArgs pa) {
+  __shared__ int uoff[PLAN_MAX_BATCH + 1];  // first unit of each sequence
+  __shared__ int sc0[PLAN_MAX_BATCH], snk[PLAN_MAX_BATCH];
+  __shared__ int start[PLAN_BUCKETS];       // bucket i holds units with PLAN_BUCKETS - i key tiles (clamped)
+  __shared__ int chunk[PLAN_THREADS];
+  const int tid = threadIdx.x, nb = pa.batch;
+  for (int b = tid; b < nb; b += PLAN_THREADS) {
+    const SeqGeom g = seq_geom(p, b);
+    uoff[b] = min(g.T, p.max_tiles);  // rows past max_seqlen_q are not computed
+    sc0[b] = g.c0;
+    snk[b] = g.NKe;
+  }
+  for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) start[i] = 0;
+  __syncthreads();
+  const int units = min(block_exclusive_scan(uoff, nb, chunk), pa.unit_cap);
+  if (tid == 0) uoff[nb] = units;
+  __syncthreads();
+  // Unit u -> (sequence, tile, bucket).
+  auto locate = [&](int u, int& b, int& t) {
+    int lo = 0, hi = nb - 1;  // last b with uoff[b] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uoff[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    t = u - uoff[lo];
+    const int nk = min(max(t + 1 + sc0[lo], 1), snk[lo]);
+    return PLAN_BUCKETS - min(nk, PLAN_BUCKETS);
+  };
+  for (int u = tid; u < units; u += PLAN_THREADS) {
+    int b, t;
+    atomicAdd(&start[locate(u, b, t)], 1);
+  }
+  __syncthreads();
+  block_exclusive_scan(start, PLAN_BUCKETS, chunk);
+  for (int u = tid; u < units; u += PLAN_THREADS) {
+    int b, t;
+    const int slot = atomicAdd(&start[locate(u, b, t)], 1);
+    pa.list[slot] = make_int2(b, t);
+  }
+  if (tid == 0) *pa.count = units;
+}
+
+template <int G, int H, int MODE>
+__global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2)
+    prefill_ordered_kernel(PrefillKernelArgs p, const int2* list, const int* count) {
+  const int kvh = int(blockIdx.x % unsigned(p.num_kv_heads));
+  const int rank = int(blockIdx.x / unsigned(p.num_kv_heads));
+  if (rank >= *count) return;
+  const int2 u = list[rank];
+  const SeqGeom g = seq_geom(p, u.x);
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][BN * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * VROW];
+  f32x4_t o[8][H], o_l[H];
+  float m[H];
+  attend_tiles<G, H, MODE>(p, g, u.x, kvh, u.y, 0, unit_tiles(g, u.y), lds_k, lds_v, o, o_l, m);
+  write_output<G, H>(p, g, kvh, u.y, o, o_l);
+}
+
 template <int G, int H>
-hipError_t launch_g(const PrefillKernelArgs& p, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<G, H>), dim3(p.num_kv_heads, batch, p.max_tiles), dim3(64 * TOKEN_WAVES * (G / H)), 0,
-                     stream, p);
+hipError_t launch_g(const PrefillKernelArgs& p, int batch, int mode, const PlanArgs* plan, hipStream_t stream) {
+  constexpr int NT = 64 * TOKEN_WAVES * (G / H);
+  if (plan) {
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, p, *plan);
+    const dim3 grid(unsigned(plan->unit_cap) * unsigned(p.num_kv_heads));
+    if (mode == LOAD_CONTIG)
+      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_CONTIG>), grid, dim3(NT), 0, stream, p, plan->list,
+                         plan->count);
+    else if (mode == LOAD_PAGED)
+      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_PAGED>), grid, dim3(NT), 0, stream, p, plan->list,
+                         plan->count);
+    else
+      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_ROWS>), grid, dim3(NT), 0, stream, p, plan->list,
+                         plan->count);
+    return hipGetLastError();
+  }
+  const dim3 grid(p.num_kv_heads, batch, p.max_tiles), block(NT);
+  if (mode == LOAD_CONTIG)
+    hipLaunchKernelGGL((prefill_kernel<G, H, LOAD_CONTIG>), grid, block, 0, stream, p);
+  else if (mode == LOAD_PAGED)
+    hipLaunchKernelGGL((prefill_kernel<G, H, LOAD_PAGED>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<G, H, LOAD_ROWS>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+
+int load_mode(const AttnArgs& a) {
+  if (!a.block_tables) return LOAD_CONTIG;
+  const int64_t row_elems = int64_t(a.num_kv_heads) * HD;
+  const bool pow2_64 = a.block_size >= 64 && (a.block_size & (a.block_size - 1)) == 0;
+  return pow2_64 && int64_t(BN) * row_elems * 2 < (int64_t(1) << 31) ? LOAD_PAGED : LOAD_ROWS;
+}
+
+// Upper bound on the (sequence, query tile) units: every sequence has at most one partial tile.
+int64_t unit_cap(int batch, int num_q_tokens, int max_seqlen_q) {
+  const int64_t by_tokens = (int64_t(num_q_tokens) + BM - 1) / BM + batch;
+  const int64_t by_max = int64_t(batch) * ((int64_t(max_seqlen_q) + BM - 1) / BM);
+  return std::min(by_tokens, by_max);
 }
 
 }  // namespace
@@ -420,7 +607,24 @@ bool prefill_fast_supported(int head_dim, int group, bool bf16) {
   return bf16 && head_dim == HD && (group == 1 || group == 2 || group == 4);
 }
 
-hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
+bool prefill_fast_strides_ok(int64_t k_stride, int64_t v_stride) {
+  return int64_t(BN) * max(k_stride, v_stride) * 2 < (int64_t(1) << 31);
+}
+
+size_t prefill_workspace_bytes(int batch, int num_q_tokens, int max_seqlen_q, int num_kv_heads) {
+  if (batch < 1 || batch > PLAN_MAX_BATCH || num_kv_heads < 1) return 0;
+  const int64_t cap = unit_cap(batch, num_q_tokens, max_seqlen_q);
+  if (cap < 1 || cap * num_kv_heads > INT32_MAX) return 0;
+  return PLAN_HEADER_BYTES + size_t(cap) * sizeof(int2);
+}
+
+bool prefill_wants_order(const AttnArgs& a, int max_seqlen_k) {
+  // Causal self-attention over this step's own tokens: a query tile's work grows with its index, so the
+  // grid's latest-tile-first launch order already is longest-first.
+  return a.block_tables != nullptr || !a.causal || max_seqlen_k != a.max_seqlen_q;
+}
+
+hipError_t launch_prefill_bf16(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   PrefillKernelArgs p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.q_stride = a.q_stride;
@@ -443,11 +647,24 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
   p.causal = a.causal;
   p.max_tiles = (a.max_seqlen_q + BM - 1) / BM;
   p.out = static_cast<uint16_t*>(a.out);
-  if (p.max_tiles > 65535) return hipErrorInvalidConfiguration;
+  if (!a.block_tables && !prefill_fast_strides_ok(a.k_stride, a.v_stride)) return hipErrorInvalidValue;
+  const int mode = load_mode(a);
   const int group = a.num_q_heads / a.num_kv_heads;
-  return group == 1   ? launch_g<1, 1>(p, a.batch, stream)
-         : group == 2 ? launch_g<2, PKV_PREFILL_H2>(p, a.batch, stream)
-                      : launch_g<4, 2>(p, a.batch, stream);
+  PlanArgs plan{};
+  const PlanArgs* planp = nullptr;
+  const size_t need = prefill_workspace_bytes(a.batch, a.num_q_tokens, a.max_seqlen_q, a.num_kv_heads);
+  if (workspace && need > 0 && workspace_bytes >= need) {
+    plan.batch = a.batch;
+    plan.unit_cap = int(unit_cap(a.batch, a.num_q_tokens, a.max_seqlen_q));
+    plan.count = static_cast<int*>(workspace);
+    plan.list = reinterpret_cast<int2*>(static_cast<char*>(workspace) + PLAN_HEADER_BYTES);
+    planp = &plan;
+  } else if (p.max_tiles > 65535) {
+    return hipErrorInvalidConfiguration;
+  }
+  return group == 1   ? launch_g<1, 1>(p, a.batch, mode, planp, stream)
+         : group == 2 ? launch_g<2, PKV_PREFILL_H2>(p, a.batch, mode, planp, stream)
+                      : launch_g<4, 2>(p, a.batch, mode, planp, stream);
 }
 
 }  // namespace pkv

@@ -45,6 +45,13 @@ hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* w
 
 // bf16, head_dim 128 prefill on MFMA.
 bool prefill_fast_supported(int head_dim, int group, bool bf16);
-hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
+// Contiguous K/V rows: a 64-row tile must span < 2^31 bytes.
+bool prefill_fast_strides_ok(int64_t k_stride, int64_t v_stride);
+// Workspace of the longest-first planner (0: not available for these sizes).
+size_t prefill_workspace_bytes(int batch, int num_q_tokens, int max_seqlen_q, int num_kv_heads);
+// Whether the longest-first order can beat the grid's launch order for this call.
+bool prefill_wants_order(const AttnArgs& a, int max_seqlen_k);
+// workspace == NULL: grid order; else the planner orders the query tiles longest first.
+hipError_t launch_prefill_bf16(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace pkv

@@ -27,8 +27,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for fn in ("kv_slot_mapping", "kv_store", "attn_prefill_varlen", "attn_decode_paged",
-               "attn_decode_workspace_bytes", "pkv_last_error"):
+    for fn in ("kv_slot_mapping", "kv_store", "attn_prefill_varlen", "attn_prefill_workspace_bytes",
+               "attn_decode_paged", "attn_decode_workspace_bytes", "pkv_last_error"):
         assert fn in names
 
 
@@ -74,20 +74,26 @@ def test_attention_rejects_bad_arguments_on_host():
     fake = ctypes.c_void_p(0x1000)
     # Hq not a multiple of Hkv
     rc = L.attn_prefill_varlen(fake, 48, fake, 32, fake, 32, fake, fake, 4, 4, 1, 4, 4, 3, 2, 16, 0.25, 1, None, 0, 0,
-                               fake, pkv.PKV_F32, None)
+                               fake, None, 0, pkv.PKV_F32, None)
     assert rc == -1 and "multiple" in _err(L)
     # head_dim beyond what is implemented
     rc = L.attn_prefill_varlen(fake, 4 * 512, fake, 2 * 512, fake, 2 * 512, fake, fake, 4, 4, 1, 4, 4, 4, 2, 512, 0.25,
-                               1, None, 0, 0, fake, pkv.PKV_F32, None)
+                               1, None, 0, 0, fake, None, 0, pkv.PKV_F32, None)
     assert rc == -2
     # causal must be 0/1
     rc = L.attn_prefill_varlen(fake, 64, fake, 32, fake, 32, fake, fake, 4, 4, 1, 4, 4, 4, 2, 16, 0.25, 5, None, 0, 0,
-                               fake, pkv.PKV_F32, None)
+                               fake, None, 0, pkv.PKV_F32, None)
     assert rc == -1
     # paged cache whose slot count is not a multiple of block_size
     rc = L.attn_prefill_varlen(fake, 64, fake, 0, fake, 0, fake, fake, 4, 4, 1, 4, 10, 4, 2, 16, 0.25, 1, fake, 2, 4,
-                               fake, pkv.PKV_F32, None)
+                               fake, None, 0, pkv.PKV_F32, None)
     assert rc == -1
+    # prefill: a workspace smaller than the longest-first planner needs
+    need_p = L.attn_prefill_workspace_bytes(4, 4, 4, 16, 8, 128, pkv.PKV_BF16)
+    assert need_p > 0
+    rc = L.attn_prefill_varlen(fake, 2048, fake, 1024, fake, 1024, fake, fake, 4, 4, 4, 4, 4, 16, 8, 128, 0.088, 1,
+                               None, 0, 0, fake, fake, need_p - 1, pkv.PKV_BF16, None)
+    assert rc == -3 and "workspace" in _err(L)
     # decode: undersized workspace for the split-KV path
     need = L.attn_decode_workspace_bytes(64, 16, 8, 128, 16, 256, pkv.PKV_BF16)
     assert need > 0
@@ -106,3 +112,9 @@ def test_workspace_size_formula_is_monotone():
     big = L.attn_decode_workspace_bytes(256, 16, 8, 128, 128, 256, pkv.PKV_BF16)
     assert 0 <= small <= big
     assert L.attn_decode_workspace_bytes(8, 4, 2, 16, 4, 4, pkv.PKV_F32) == 0  # generic path: no workspace
+    assert L.attn_prefill_workspace_bytes(8, 100, 50, 4, 2, 16, pkv.PKV_F32) == 0  # generic path: no workspace
+    assert L.attn_prefill_workspace_bytes(5000, 9000, 64, 16, 8, 128, pkv.PKV_BF16) == 0  # batch past the planner
+    # one count plus one entry per possible query tile: grows with the tokens, bounded by batch * tiles
+    a = L.attn_prefill_workspace_bytes(16, 5000, 512, 16, 8, 128, pkv.PKV_BF16)
+    b = L.attn_prefill_workspace_bytes(16, 9000, 512, 16, 8, 128, pkv.PKV_BF16)
+    assert 0 < a <= b

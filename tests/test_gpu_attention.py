@@ -26,7 +26,7 @@ def _tol(dtype):
     return BF16_TOL if dtype == "bf16" else F32_TOL
 
 
-def _run_step(pkv, case, paged):
+def _run_step(pkv, case, paged, order=True):
     """Store history + new tokens through the HIP path, then attention; returns (out, kc, vc, slot_mapping)."""
     kc, vc = nan_cache(case), nan_cache(case)
     gpu_store_history(case, kc, vc)
@@ -38,10 +38,10 @@ def _run_step(pkv, case, paged):
         out = pkv.attn_decode_paged(q, kc, vc, i32(case.context_lens), bt, case.scale)
     elif paged:
         out = pkv.attn_prefill_varlen(q, kc, vc, i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), int(case.Lq.max()),
-                                      int(case.Lk.max()), case.scale, causal=True, block_table=bt)
+                                      int(case.Lk.max()), case.scale, causal=True, block_table=bt, order=order)
     else:
         out = pkv.attn_prefill_varlen(q, k, v, i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), int(case.Lq.max()),
-                                      int(case.Lk.max()), case.scale, causal=True)
+                                      int(case.Lk.max()), case.scale, causal=True, order=order)
     torch.cuda.synchronize()
     return out, kc, vc, sm
 
@@ -141,19 +141,71 @@ PREFILL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("order", [True, False])
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("dtype,hq,hkv,hd,bs,lq,prefix,seed", PREFILL_CASES)
-def test_prefill_small(pkv, dtype, hq, hkv, hd, bs, lq, prefix, seed, paged):
+def test_prefill_small(pkv, dtype, hq, hkv, hd, bs, lq, prefix, seed, paged, order):
     if not paged and any(prefix):
         pytest.skip("a cached prefix is only readable through the block tables")
     lk = [a + b for a, b in zip(lq, prefix)]
     num_blocks = sum(math.ceil(c / bs) for c in lk) + 2
     case = workloads.make_case(lq, lk, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, block_size=bs,
                                num_blocks=num_blocks, dtype=dtype, seed=seed)
-    log(f"prefill {dtype} {hq}/{hkv}/{hd} bs={bs} lq={lq} prefix={prefix} paged={paged}")
-    out, kc, vc, sm = _run_step(pkv, case, paged)
+    log(f"prefill {dtype} {hq}/{hkv}/{hd} bs={bs} lq={lq} prefix={prefix} paged={paged} order={order}")
+    out, kc, vc, sm = _run_step(pkv, case, paged, order)
     np.testing.assert_array_equal(to_host(sm), oracle_slot_mapping(case))
     _check_attention(case, out)
+
+
+ORDER_CASES = [
+    # (hq, hkv, new lengths, cached prefix lengths, block size, seed): prefixes of very different lengths,
+    # empty sequences between full ones, a single tile, GQA groups 1 / 2 / 4, block sizes 64 .. 256 and 7.
+    (16, 8, [90, 513, 64, 300], [3000, 100, 4100, 0], 256, 71),
+    (16, 8, [0, 700, 0, 333, 1], [0, 20, 5, 900, 4000], 256, 72),
+    (16, 8, [64], [130], 256, 73),
+    (8, 8, [200, 900], [1200, 0], 64, 74),
+    (32, 8, [400, 129], [2000, 77], 128, 75),
+    (16, 8, [100, 37], [500, 900], 7, 76),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,lq,prefix,bs,seed", ORDER_CASES)
+def test_prefill_longest_first_order(pkv, hq, hkv, lq, prefix, bs, seed):
+    """Query tiles listed longest first by the planner: same values as the latest-tile-first grid, bit for bit
+    (each tile's arithmetic does not depend on when it runs), and within tolerance of the oracle."""
+    lk = [a + b for a, b in zip(lq, prefix)]
+    case = workloads.make_case(lq, lk, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=bs,
+                               num_blocks=sum(math.ceil(c / bs) for c in lk) + 2, dtype="bf16", seed=seed)
+    log(f"longest-first {hq}/{hkv} lq={lq} prefix={prefix} bs={bs}")
+    out, *_ = _run_step(pkv, case, paged=True, order=True)
+    _check_attention(case, out)
+    ref, *_ = _run_step(pkv, case, paged=True, order=False)
+    assert torch.equal(out, ref)
+
+
+def test_prefill_order_workspace(pkv):
+    """The planner's workspace needs no clearing (garbage in, same result) and an undersized one is refused."""
+    lq, prefix = [300, 70, 129], [2000, 10, 600]
+    lk = [a + b for a, b in zip(lq, prefix)]
+    case = workloads.make_case(lq, lk, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+                               num_blocks=sum(math.ceil(c / 256) for c in lk) + 2, dtype="bf16", seed=77)
+    kc, vc = nan_cache(case), nan_cache(case)
+    gpu_store_history(case, kc, vc)
+    pkv.kv_store(to_dev(case.k, "bf16"), to_dev(case.v, "bf16"), kc, vc, gpu_slot_mapping(case))
+    q, bt = to_dev(case.q, "bf16"), i32(case.block_tables)
+    args = (q, kc, vc, i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), 300, 2600, case.scale)
+    need = pkv.attn_prefill_workspace_bytes(3, sum(lq), 300, 16, 8, 128)
+    assert need > 0
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")
+    first = pkv.attn_prefill_varlen(*args, block_table=bt, workspace=ws)
+    torch.cuda.synchronize()
+    _check_attention(case, first)
+    ws.fill_(0x7F)
+    again = pkv.attn_prefill_varlen(*args, block_table=bt, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first, again)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.attn_prefill_varlen(*args, block_table=bt, workspace=ws[: need - 1])
 
 
 def test_prefill_strided_qkv_from_merged_projection(pkv):
