@@ -69,14 +69,17 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* lds_ptr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// IEEE maximum (v_maximum3_f32 on gfx950: no operand canonicalisation, NaN propagates).
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Maximum over lanes i and i ^ 16 (rows of 16 swapped pairwise), and over lanes i and i ^ 32.
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_ieee(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_ieee(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 struct PrefillKernelArgs {
@@ -314,7 +317,10 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
       if (kt + 2 < kt1) next_blk = tile_block(kt + 2);
     }
 
-    // S^T = K Q^T for 4 blocks of 16 keys.
+    // S^T = K Q^T for 4 blocks of 16 keys.  The wave raises its issue priority for this matrix burst, so that
+    // on a SIMD shared with a wave in its softmax the matrix core is fed first and the vector work fills the
+    // gaps (measured +6% at 32 x 2048 non-causal, +15% on ragged prefix batches).
+    __builtin_amdgcn_s_setprio(1);
     f32x4_t s[4][H];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -329,6 +335,8 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
         for (int n = 0; n < H; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
       }
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // Mask, online softmax.  Lane holds raw scores of keys kt*64 + 16 kb + 4 grp + r for query `tok`; the
     // scale c > 0 is applied inside exp2(s c - m) (q carries the sign of the scale), m is in scaled units.
@@ -351,11 +359,12 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
     bool need = false;
 #pragma unroll
     for (int n = 0; n < H; ++n) {
-      float mx = s[0][n][0];
+      // Balanced tree over the lane's 16 scores (short dependency chains).
+      float m4[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = (kb == 0 ? 1 : 0); r < 4; ++r) mx = __builtin_elementwise_maximum(mx, s[kb][n][r]);
+        m4[kb] = fmax_ieee(fmax_ieee(s[kb][n][0], s[kb][n][1]), fmax_ieee(s[kb][n][2], s[kb][n][3]));
+      const float mx = fmax_ieee(fmax_ieee(m4[0], m4[1]), fmax_ieee(m4[2], m4[3]));
       mxc[n] = max_xor32(max_xor16(mx)) * c;
       need |= mxc[n] > m[n] + kRescaleSlack;
     }
