@@ -8,9 +8,11 @@ whole step's time.  Steps rotate over ``--layers`` independent caches (different
 the 256 MB Infinity Cache cannot hold the working set between steps.
 
 The same JSON line carries:
-  roofline      the decode attention call (split + combine kernels) timed with HIP events on the stream it
-                runs on, against MI355X's 8 TB/s HBM peak; ``traffic`` from rocprofv3 counters kept in
-                profiles/ (null if the kernel source changed since they were taken);
+  roofline      the decode attention call (split + combine kernels) timed with two HIP events on the stream
+                it runs on around K back-to-back calls over the same rotated caches (an event record per
+                call would make the GPU drain before each one), against MI355X's 8 TB/s HBM peak;
+                ``traffic`` from rocprofv3 counters kept in profiles/ (null if the kernel source changed
+                since they were taken);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, BLAS pinned to one thread;
   secondary     varlen prefill TFLOP/s (workload 3), prefix-cache prefill TFLOP/s (workload 4), the store
                 sweep GB/s (workload 5, N=16384) and the long padded decode GB/s (workload 5, batch 256).
@@ -61,38 +63,31 @@ def measured_traffic(name, src_hash):
 
 # ------------------------------------------------------------------------------------------------ GPU side
 
-class Timer:
-    """HIP events on the current stream around one call per step."""
-
-    def __init__(self, torch, n):
-        self.torch = torch
-        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        self.i = 0
-
-    def __enter__(self):
-        self.pairs[self.i][0].record()
-        return self
-
-    def __exit__(self, *exc):
-        self.pairs[self.i][1].record()
-        self.i += 1
-
-    def mean_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.pairs[: self.i]) / max(self.i, 1)
-
-
 def run_steps(torch, step, steps, warmup):
-    """W untimed steps, then exactly K timed steps between device synchronisations."""
+    """W untimed steps, then exactly K timed steps between device synchronisations; returns ms per step."""
     for i in range(warmup):
-        step(i, None)
+        step(i)
     torch.cuda.synchronize()
-    timer = Timer(torch, steps)
     t0 = time.perf_counter()
     for i in range(steps):
-        step(warmup + i, timer)
+        step(warmup + i)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    return wall_ms, timer.mean_ms()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_kernel(torch, call, n):
+    """HIP events on the current stream around ``n`` back-to-back calls (no event between them: an event
+    record waits for the GPU to drain, which would add its own gap to every call); returns ms per call."""
+    for i in range(2):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(n):
+        call(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n
 
 
 def dev_case_layers(make, layers, torch):
@@ -141,18 +136,21 @@ def bench_decode(pkv, torch, make, steps, warmup, layers):
     outs = [torch.empty_like(c.q) for c in cases]
     torch.cuda.synchronize()
 
-    def step(i, timer):
-        L = i % layers
+    def store(L):
         c, (kc, vc) = cases[L], caches[L]
         pkv.kv_slot_mapping(meta["bt"], c0.block_size, c0.batch, context_lens=meta["ctx"], out=sm)
         pkv.kv_store(c.k, c.v, kc, vc, sm)
-        if timer is None:
-            pkv.attn_decode_paged(c.q, kc, vc, meta["ctx"], meta["bt"], c0.scale, out=outs[L], workspace=ws)
-        else:
-            with timer:
-                pkv.attn_decode_paged(c.q, kc, vc, meta["ctx"], meta["bt"], c0.scale, out=outs[L], workspace=ws)
 
-    wall_ms, kern_ms = run_steps(torch, step, steps, warmup)
+    def attend(L):
+        c, (kc, vc) = cases[L], caches[L]
+        pkv.attn_decode_paged(c.q, kc, vc, meta["ctx"], meta["bt"], c0.scale, out=outs[L], workspace=ws)
+
+    def step(i):
+        store(i % layers)
+        attend(i % layers)
+
+    wall_ms = run_steps(torch, step, steps, warmup)
+    kern_ms = time_kernel(torch, lambda i: attend(i % layers), steps)
     kv_bytes = int(c0.Lk.astype(int).sum()) * 2 * c0.num_kv_heads * c0.head_dim * 2
     del caches, cases
     torch.cuda.empty_cache()
@@ -186,18 +184,15 @@ def bench_prefill(pkv, torch, make, steps, warmup, layers, paged):
         else:
             pkv.attn_prefill_varlen(c.q, c.k, c.v, cu_q, cu_k, mq, mk, c0.scale, out=outs[L])
 
-    def step(i, timer):
+    def step(i):
         L = i % layers
         c, (kc, vc) = cases[L], caches[L]
         pkv.kv_slot_mapping(bt, c0.block_size, n, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, out=sm)
         pkv.kv_store(c.k, c.v, kc, vc, sm)
-        if timer is None:
-            attn(c, kc, vc, L)
-        else:
-            with timer:
-                attn(c, kc, vc, L)
+        attn(c, kc, vc, L)
 
-    wall_ms, kern_ms = run_steps(torch, step, steps, warmup)
+    wall_ms = run_steps(torch, step, steps, warmup)
+    kern_ms = time_kernel(torch, lambda i: attn(cases[i % layers], *caches[i % layers], i % layers), steps)
     flops = prefill_flops(c0)
     del caches, cases
     torch.cuda.empty_cache()
@@ -213,15 +208,12 @@ def bench_store(pkv, torch, steps, warmup):
     slots = [torch.from_numpy(s).cuda() for s in sw.slots]
     torch.cuda.synchronize()
 
-    def step(i, timer):
+    def step(i):
         s = i % len(slots)
-        if timer is None:
-            pkv.kv_store(sw.key[s], sw.value[s], kc, vc, slots[s])
-        else:
-            with timer:
-                pkv.kv_store(sw.key[s], sw.value[s], kc, vc, slots[s])
+        pkv.kv_store(sw.key[s], sw.value[s], kc, vc, slots[s])
 
-    wall_ms, kern_ms = run_steps(torch, step, steps, warmup)
+    wall_ms = run_steps(torch, step, steps, warmup)
+    kern_ms = time_kernel(torch, step, steps)
     n = len(sw.slots[0])
     row = sw.num_kv_heads * sw.head_dim * 2
     moved = 2 * n * row * 2 + 4 * n  # read + write of K and V rows, plus the slots
@@ -300,7 +292,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic("attn_decode_workload2", dec_hash),
-                "kernel": "attn_decode_paged (split + combine kernels)", "kernel_ms": round(dec["kernel_ms"], 5),
+                "kernel": "attn_decode_paged (decode_lean_kernel + decode_combine_kernel)", "kernel_ms": round(dec["kernel_ms"], 5),
                 "algorithmic_bytes": dec["kv_bytes"], "source_hash": dec_hash}
 
     secondary = {}

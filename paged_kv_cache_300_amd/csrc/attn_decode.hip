@@ -7,10 +7,10 @@
 //
 // How (gfx950 design, not the pages' library call):
 //  * Even split of the whole batch: the keys of all sequences, laid end to end (T = sum of context
-//    lengths), are cut into W equal ranges, one per worker, with W x (kv-head groups) = the number of
-//    work-groups the 256 CUs hold at once.  Every work-group therefore streams the same number of bytes and the launch is a
-//    single round with no tail, whatever the mix of context lengths (a range may cover the end of one
-//    sequence and the start of the next).
+//    lengths), are cut into W equal ranges, one per worker (two workers per CU, each worker one work-group
+//    per group of 4 kv heads, all resident at once).  Every work-group therefore streams the same number of
+//    bytes and the launch is a single round with no tail, whatever the mix of context lengths (a range may
+//    cover the end of one sequence and the start of the next).
 //  * A work-group has one wave per kv head, so together its waves read whole contiguous token rows of the
 //    cache; each wave serves every query head of its kv head's GQA group, so each K/V row is read from HBM
 //    once for the whole group.
@@ -109,7 +109,41 @@ __device__ __forceinline__ int worker_of(int64_t T, int W, int64_t x) { return i
 template <int G>
 __global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKernelArgs p) {
   const int w = blockIdx.y, W = p.workers;
-  const int64_t T = p.cu[p.batch];
+  // Prefix sums of the clamped context lengths.  Up to LDS_CU_MAX - 1 sequences every work-group scans them
+  // into LDS itself (a few hundred cycles, and one kernel launch less); the first work-group also stores them
+  // for the combine kernel.  Larger batches read the sums decode_prefix_kernel wrote.
+  extern __shared__ int64_t s_cu[];
+  const bool cu_in_lds = p.batch + 1 <= LDS_CU_MAX;
+  if (cu_in_lds) {
+    int64_t* chunk = s_cu + (p.batch + 1);
+    const int nt = blockDim.x, tid = threadIdx.x;
+    const int per = (p.batch + nt - 1) / nt;
+    const int c0 = min(tid * per, p.batch), c1 = min(c0 + per, p.batch);
+    int64_t acc = 0;
+    for (int i = c0; i < c1; ++i) {
+      const int64_t c = clamp_ctx(p, i);
+      s_cu[i + 1] = c;
+      acc += c;
+    }
+    chunk[tid] = acc;
+    __syncthreads();
+    for (int off = 1; off < nt; off <<= 1) {
+      const int64_t y = tid >= off ? chunk[tid - off] : 0;
+      __syncthreads();
+      chunk[tid] += y;
+      __syncthreads();
+    }
+    acc = tid > 0 ? chunk[tid - 1] : 0;
+    for (int i = c0; i < c1; ++i) {
+      acc += s_cu[i + 1];
+      s_cu[i + 1] = acc;
+    }
+    if (tid == 0) s_cu[0] = 0;
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      for (int i = tid; i <= p.batch; i += nt) p.cu[i] = s_cu[i];
+  }
+  const int64_t T = cu_in_lds ? s_cu[p.batch] : p.cu[p.batch];
   int64_t x = range_begin(T, W, w);
   const int64_t x_end = range_begin(T, W, w + 1);
   if (x >= x_end) return;
@@ -122,14 +156,7 @@ __global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKerne
   const uint16_t* kbase = p.kc + kvh * HD + sub * 8;
   const uint16_t* vbase = p.vc + kvh * HD + sub * 8;
 
-  // First sequence of the range: the last b with cu[b] <= x (empty sequences are skipped over).  The prefix
-  // sums are staged in LDS when they fit, so the search costs one global round trip instead of log2(batch).
-  extern __shared__ int64_t s_cu[];
-  const bool cu_in_lds = p.batch + 1 <= LDS_CU_MAX;
-  if (cu_in_lds) {
-    for (int i = threadIdx.x; i <= p.batch; i += blockDim.x) s_cu[i] = p.cu[i];
-    __syncthreads();
-  }
+  // First sequence of the range: the last b with cu[b] <= x (empty sequences are skipped over).
   int b;
   {
     int lo = 0, hi = p.batch;  // cu[lo] <= x < cu[hi]
@@ -387,11 +414,23 @@ int resident_workers(const void* kernel, int threads, int key) {
   if (slot > 0) return slot;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, LDS_CU_MAX * sizeof(int64_t)) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads,
+                                                   (LDS_CU_MAX + 64 * MAX_WAVES) * sizeof(int64_t)) !=
           hipSuccess || per_cu <= 0)
     per_cu = 1;
   slot = std::min(MAX_WORKERS, cus * per_cu);
   return slot;
+}
+
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cached[dev] = cus;
+  return cus;
 }
 
 template <int G, int KEY>
@@ -399,12 +438,15 @@ hipError_t launch_g(DecodeKernelArgs& p, hipStream_t stream) {
   const int waves = std::min(MAX_WAVES, p.num_kv_heads);
   const int threads = 64 * waves;
   const int head_groups = (p.num_kv_heads + waves - 1) / waves;
-  // One resident round in total: W workers x head_groups work-groups, the head groups of a worker adjacent
-  // in launch order so they read the two halves of the same token rows at the same time.
+  // W workers x head_groups work-groups, the head groups of a worker adjacent in launch order so they read the
+  // two halves of the same token rows at the same time.  W = 2 per CU, within one resident round: enough
+  // loads in flight to saturate HBM (measured on MI355X, batch 64: 1024 / 768 / 512 / 256 workers reach
+  // 4.93 / 5.07 / 5.14 / 4.99 TB/s; fewer workers also mean fewer partial outputs to merge).
   const int resident = resident_workers(reinterpret_cast<const void*>(&decode_lean_kernel<G>), threads, KEY);
-  p.workers = std::max(1, resident / head_groups);
-  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, p);
-  const size_t lds = p.batch + 1 <= LDS_CU_MAX ? size_t(p.batch + 1) * sizeof(int64_t) : 0;
+  p.workers = std::max(1, std::min(resident / head_groups, 2 * device_cus()));
+  const bool cu_in_lds = p.batch + 1 <= LDS_CU_MAX;
+  if (!cu_in_lds) hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, p);
+  const size_t lds = cu_in_lds ? size_t(p.batch + 1 + threads) * sizeof(int64_t) : 0;
   hipLaunchKernelGGL(decode_lean_kernel<G>, dim3(head_groups, p.workers), dim3(threads), lds, stream, p);
   hipLaunchKernelGGL(decode_combine_kernel, dim3(p.num_q_heads, p.batch), dim3(HD), 0, stream, p);
   return hipGetLastError();

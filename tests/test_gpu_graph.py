@@ -1,0 +1,103 @@
+"""HIP-graph capture of the hot path: a decode step (kv_slot_mapping + kv_store + attn_decode_paged) and a
+prefix-cache prefill call captured once and replayed several times, with eager work and synchronisations
+between the replays; every replay must equal the eager result bit for bit, and the eager result matches the
+oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import gpu_slot_mapping, gpu_store_history, i32, log, max_abs_err, nan_cache, oracle_attention, to_dev, to_host
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_300_amd as m
+    m.lib()
+    return m
+
+
+def _graph(fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def test_decode_step_graph_replays(pkv):
+    ctx = np.array([700, 1, 0, 2049, 300, 4096, 0, 77])  # padding rows (context 0, slot -1) included
+    case = workloads.decode_case(ctx, num_blocks=int(sum(math.ceil(c / 256) for c in ctx)) + 2, seed=91,
+                                 max_blocks=16)
+    kc, vc = nan_cache(case), nan_cache(case)
+    gpu_store_history(case, kc, vc)
+    k, v, q = (to_dev(x, "bf16") for x in (case.k, case.v, case.q))
+    bt, cl = i32(case.block_tables), i32(case.context_lens)
+    sm = torch.empty(case.batch, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(pkv.attn_decode_workspace_bytes(case.batch, 16, 8, 128, 16, 256), 1), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(q)
+
+    def step():
+        pkv.kv_slot_mapping(bt, 256, case.batch, context_lens=cl, out=sm)
+        pkv.kv_store(k, v, kc, vc, sm)
+        pkv.attn_decode_paged(q, kc, vc, cl, bt, case.scale, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    want = oracle_attention(case)
+    got = oracle.as_f64(to_host(eager), "bf16")
+    err = max(max_abs_err(got[b:b + 1], w) for b, w in want.items())
+    log(f"eager decode max-abs {err:.3e}")
+    assert err <= 2e-2
+    g = _graph(step)
+    for rep in range(4):
+        out.fill_(7.0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+        scratch = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager kernels on the same stream
+        torch.cuda.synchronize()
+        del scratch
+
+
+def test_prefix_prefill_graph_replays(pkv):
+    lq, prefix = [200, 64, 1], [1000, 0, 3000]
+    lk = [a + b for a, b in zip(lq, prefix)]
+    case = workloads.make_case(lq, lk, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+                               num_blocks=sum(math.ceil(c / 256) for c in lk) + 2, dtype="bf16", seed=92)
+    kc, vc = nan_cache(case), nan_cache(case)
+    gpu_store_history(case, kc, vc)
+    pkv.kv_store(to_dev(case.k, "bf16"), to_dev(case.v, "bf16"), kc, vc, gpu_slot_mapping(case))
+    q = to_dev(case.q, "bf16")
+    cu_q, cu_k, bt = i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), i32(case.block_tables)
+    ws = torch.empty(pkv.attn_prefill_workspace_bytes(3, sum(lq), 200, 16, 8, 128), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+
+    def call():
+        pkv.attn_prefill_varlen(q, kc, vc, cu_q, cu_k, 200, max(lk), case.scale, block_table=bt, out=out,
+                                workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = _graph(call)
+    for rep in range(4):
+        out.zero_()
+        ws.fill_(0xEE)                      # the planner's workspace needs no clearing
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+    want = oracle_attention(case)
+    got = oracle.as_f64(to_host(eager), "bf16")
+    err = max(max_abs_err(got[int(case.cu_seqlens_q[b]):int(case.cu_seqlens_q[b + 1])], w) for b, w in want.items())
+    log(f"prefill eager max-abs {err:.3e}")
+    assert err <= 2e-2
