@@ -16,7 +16,8 @@
 //    once for the whole group.
 //  * A token's 256-byte K (or V) row for one kv head is read by 8 lanes, 2 x 16 bytes each; a wave reads
 //    8 tokens per instruction (8 full 128-byte lines) and 32 tokens per iteration, all loads issued before
-//    any arithmetic; the block-table entries of the next iteration are fetched one iteration ahead.
+//    any arithmetic; the block-table entries of the next iteration are fetched one iteration ahead.  The
+//    cache is read with non-temporal loads (each byte is used once): measured 5.2 -> 5.6 TB/s at batch 64.
 //  * q.k uses the packed bf16 dot instruction (exact products, float32 sums); the 8 partial sums of a
 //    token are combined with three DPP moves inside the 8-lane group.
 //  * Each 8-lane group runs its own online softmax (running max m, normaliser l, unnormalised output) over
@@ -233,10 +234,10 @@ __global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKerne
       for (int u = 0; u < 4; ++u) {
         const int64_t off = slot_n[u] * slot_elems;
         ok[u] = ok_n[u];
-        ka[u] = *reinterpret_cast<const u32x4*>(kbase + off);
-        kb[u] = *reinterpret_cast<const u32x4*>(kbase + off + 64);
-        va[u] = *reinterpret_cast<const u32x4*>(vbase + off);
-        vb[u] = *reinterpret_cast<const u32x4*>(vbase + off + 64);
+        ka[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
+        kb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off + 64));
+        va[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
+        vb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off + 64));
       }
       if (base + WAVE_TOKENS < t1) locate(base + WAVE_TOKENS);
 
