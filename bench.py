@@ -255,7 +255,7 @@ def _time_oracle_step(case, kc, vc, min_seconds):
         oracle.decode_ref(oracle.as_f64(case.q, "bf16"), oracle.as_f64(kc2, "bf16"), oracle.as_f64(vc2, "bf16"),
                           case.context_lens, case.block_tables, 256, case.scale)
         reps += 1
-        if time.perf_counter() - t0 >= min_seconds or reps >= 50:
+        if time.perf_counter() - t0 >= min_seconds or reps >= 1000:
             break
     return reps, (time.perf_counter() - t0) / reps
 
