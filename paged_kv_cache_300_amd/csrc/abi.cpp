@@ -139,7 +139,7 @@ int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t 
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.ctx_lens = nullptr;
   a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq; a.block_size = paged ? block_size : 1;
   a.num_k_rows = num_k_rows; a.num_blocks = num_blocks;
-  a.batch = batch; a.max_seqlen_q = max_seqlen_q; a.num_q_tokens = num_q_tokens;
+  a.batch = batch; a.max_seqlen_q = max_seqlen_q; a.max_seqlen_k = max_seqlen_k; a.num_q_tokens = num_q_tokens;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
   a.scale = softmax_scale; a.causal = causal; a.out = out;
   const bool bf16 = dtype == PKV_BF16;
@@ -151,7 +151,7 @@ int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t 
       const size_t need = pkv::prefill_workspace_bytes(batch, num_q_tokens, max_seqlen_q, num_kv_heads);
       if (need > 0 && workspace_bytes < need)
         return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-      if (need == 0 || !pkv::prefill_wants_order(a, max_seqlen_k)) workspace = nullptr;
+      if (need == 0 || !pkv::prefill_wants_order(a)) workspace = nullptr;
     }
     return hip_status(pkv::launch_prefill_bf16(a, workspace, workspace_bytes, stream),
                       "attn_prefill_varlen launch");

@@ -26,6 +26,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -310,16 +311,22 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
   store_tile(st, lds_k[0], lds_v[0], tid);
   __syncthreads();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
+  // One key tile.  Scores are formed in two halves of 32 keys; the exponentials of the first half are taken
+  // with the current reference maximum while the second half's products are still on the matrix core (redone
+  // in the rare tiles where the reference moves), and the second half's exponentials run while the first
+  // half's P V products execute, so a wave keeps its matrix core and vector unit busy together.  MASKED:
+  // the tile crosses the causal diagonal or the end of the keys (only the last one or two tiles of a row).
+  auto tile_step = [&](auto masked_tag, int kt) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = (kt - kt0) & 1;
     if (kt + 1 < kt1) {
       st = load_tile<MODE, CH>(p, src, kt + 1, next_blk);
       if (kt + 2 < kt1) next_blk = tile_block(kt + 2);
     }
 
-    // S^T = K Q^T for 4 blocks of 16 keys.  The wave raises its issue priority for this matrix burst, so that
-    // on a SIMD shared with a wave in its softmax the matrix core is fed first and the vector work fills the
-    // gaps (measured +6% at 32 x 2048 non-causal, +15% on ragged prefix batches).
+    // S^T = K Q^T, keys 0-31 (blocks kb 0, 1) then 32-63 (kb 2, 3).  The wave raises its issue priority for
+    // this matrix burst, so that on a SIMD shared with a wave in its softmax the matrix core is fed first
+    // (measured +6% at 32 x 2048 non-causal, +15% on ragged prefix batches).
     __builtin_amdgcn_s_setprio(1);
     f32x4_t s[4][H];
 #pragma unroll
@@ -327,21 +334,21 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
 #pragma unroll
       for (int n = 0; n < H; ++n) s[kb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&lds_k[buf][(kb * 16 + col) * KROW + ks * 32 + grp * 8]);
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int n = 0; n < H; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
+        for (int kb = 2 * half; kb < 2 * half + 2; ++kb) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(&lds_k[buf][(kb * 16 + col) * KROW + ks * 32 + grp * 8]);
+#pragma unroll
+          for (int n = 0; n < H; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
+        }
       }
-    }
-
     __builtin_amdgcn_s_setprio(0);
 
-    // Mask, online softmax.  Lane holds raw scores of keys kt*64 + 16 kb + 4 grp + r for query `tok`; the
-    // scale c > 0 is applied inside exp2(s c - m) (q carries the sign of the scale), m is in scaled units.
-    const bool need_mask = (kt + 1) * BN > Lk || (p.causal && (kt + 1) * BN - 1 > qpos0);
-    if (need_mask) {
+    // Lane holds raw scores of keys kt*64 + 16 kb + 4 grp + r for query `tok`; the scale c > 0 is applied
+    // inside exp2(s c - m) (q carries the sign of the scale), m is in scaled units.
+    if constexpr (MASKED) {
       const int room = lim - (kt * BN + grp * 4);  // key kt*64 + 4 grp + 16 kb + r is visible iff 16 kb + r <= room
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -359,7 +366,7 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
     bool need = false;
 #pragma unroll
     for (int n = 0; n < H; ++n) {
-      // Balanced tree over the lane's 16 scores (short dependency chains).
+      // Balanced trees over the lane's 16 scores (short dependency chains), the first half's first.
       float m4[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -368,6 +375,15 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
       mxc[n] = max_xor32(max_xor16(mx)) * c;
       need |= mxc[n] > m[n] + kRescaleSlack;
     }
+    // First half's weights with the current reference, taken while the second half's products run.  In the
+    // rare tiles where the reference moves they are redone: the half's scores are formed again (K and Q are
+    // still at hand) and weighted with the new reference, since the old one may lie far below (first tile).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int n = 0; n < H; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[kb][n][r] = fast_exp2(fmaf(s[kb][n][r], c, -m[n]));
     if (__any(need)) {
 #pragma unroll
       for (int n = 0; n < H; ++n) {
@@ -378,30 +394,59 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
 #pragma unroll
         for (int d = 0; d < 8; ++d) o[d][n] *= alpha;
       }
-    }
-    u32x4 pb[H][2];
 #pragma unroll
-    for (int n = 0; n < H; ++n) {
-      float pv[4][4];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int n = 0; n < H; ++n) s[kb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[kb][r] = fast_exp2(fmaf(s[kb][n][r], c, -m[n]));
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        pb[n][h].x = pack_bf16x2(pv[2 * h][0], pv[2 * h][1]);
-        pb[n][h].y = pack_bf16x2(pv[2 * h][2], pv[2 * h][3]);
-        pb[n][h].z = pack_bf16x2(pv[2 * h + 1][0], pv[2 * h + 1][1]);
-        pb[n][h].w = pack_bf16x2(pv[2 * h + 1][2], pv[2 * h + 1][3]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(&lds_k[buf][(kb * 16 + col) * KROW + ks * 32 + grp * 8]);
+#pragma unroll
+          for (int n = 0; n < H; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
+        }
+      if constexpr (MASKED) {
+        const int room = lim - (kt * BN + grp * 4);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool vis = kb * 16 + r <= room;
+#pragma unroll
+            for (int n = 0; n < H; ++n) s[kb][n][r] = vis ? s[kb][n][r] : -INFINITY;
+          }
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int n = 0; n < H; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[kb][n][r] = fast_exp2(fmaf(s[kb][n][r], c, -m[n]));
     }
 
-    // O^T += V^T P^T.  A operand = V^T: lane (col, grp) needs V[key][16 d + col] for the keys of its P^T slots,
-    // {4 grp + j} and {16 + 4 grp + j} (j < 4) of each 32-key half.  ds_read_b64_tr_b16 transposes 16x4 blocks
-    // inside each quarter-wave: source lane 4 j + q supplies V[key j][dim0 + 4 q .. + 3] and result lane i
-    // receives V[key j][dim0 + i] for j = 0..3.
+    // O^T += V^T P^T, one 32-key half at a time.  A operand = V^T: lane (col, grp) needs V[key][16 d + col]
+    // for the keys of its P^T slots, {4 grp + j} and {16 + 4 grp + j} (j < 4) of the half.
+    // ds_read_b64_tr_b16 transposes 16x4 blocks inside each quarter-wave: source lane 4 j + q supplies
+    // V[key j][dim0 + 4 q .. + 3] and result lane i receives V[key j][dim0 + i] for j = 0..3.
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      if (h == 1) {
+#pragma unroll
+        for (int kb = 2; kb < 4; ++kb)
+#pragma unroll
+          for (int n = 0; n < H; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[kb][n][r] = fast_exp2(fmaf(s[kb][n][r], c, -m[n]));
+      }
+      u32x4 pb[H];
+#pragma unroll
+      for (int n = 0; n < H; ++n) {
+        pb[n].x = pack_bf16x2(s[2 * h][n][0], s[2 * h][n][1]);
+        pb[n].y = pack_bf16x2(s[2 * h][n][2], s[2 * h][n][3]);
+        pb[n].z = pack_bf16x2(s[2 * h + 1][n][0], s[2 * h + 1][n][1]);
+        pb[n].w = pack_bf16x2(s[2 * h + 1][n][2], s[2 * h + 1][n][3]);
+      }
       const int row = h * 32 + grp * 4 + (col >> 2);
       const uint16_t* vrow = &lds_v[buf][row * VROW + (col & 3) * 4];
 #pragma unroll
@@ -410,15 +455,22 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
         const u32x2 hi = ds_read_tr16(vrow + 16 * VROW + d * 16);
         const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int n = 0; n < H; ++n) o[d][n] = mfma_16x16x32(a, pb[n][h], o[d][n]);
+        for (int n = 0; n < H; ++n) o[d][n] = mfma_16x16x32(a, pb[n], o[d][n]);
       }
 #pragma unroll
-      for (int n = 0; n < H; ++n) o_l[n] = mfma_16x16x32(ones, pb[n][h], o_l[n]);
+      for (int n = 0; n < H; ++n) o_l[n] = mfma_16x16x32(ones, pb[n], o_l[n]);
     }
 
     if (kt + 1 < kt1) store_tile(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
     __syncthreads();
-  }
+  };
+
+  // Tiles kt >= kt_mask need a mask: (kt + 1) * 64 > Lk, or (causal) (kt + 1) * 64 - 1 > qpos0.
+  int kt_mask = Lk / BN;
+  if (p.causal) kt_mask = min(kt_mask, qpos0 + 1 > 0 ? (qpos0 + 1) / BN : 0);
+  kt_mask = min(max(kt_mask, kt0), kt1);
+  for (int kt = kt0; kt < kt_mask; ++kt) tile_step(std::integral_constant<bool, false>(), kt);
+  for (int kt = kt_mask; kt < kt1; ++kt) tile_step(std::integral_constant<bool, true>(), kt);
 }
 
 // Normalise and write: lane holds dims 16 d + 4 grp + r of query `tok`, head kvh*G + hb + n.
@@ -472,19 +524,20 @@ __global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(
 // largest first, and the ordered kernel takes unit `rank` = its launch index / Hkv: the hardware hands out work-
 // groups in launch order, so the longest rows start first and the short ones fill the tail (greedy
 // longest-processing-time scheduling, with no communication between work-groups).
-constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_THREADS = 256;
 constexpr int PLAN_MAX_BATCH = 4096;
-constexpr int PLAN_BUCKETS = 4096;  // units with more key tiles share the last bucket
+constexpr int PLAN_BUCKETS = 4096;  // at most; units with more key tiles share the last bucket
 constexpr size_t PLAN_HEADER_BYTES = 256;
 
 struct PlanArgs {
   int batch;
+  int buckets;   // key-tile counts 1 .. buckets (larger counts share the last), from max_seqlen_k
   int unit_cap;  // list capacity; units past it are dropped (the host sizes it from num_q_tokens)
   int2* list;    // [unit_cap] (sequence, query tile), longest first
   int* count;    // number of listed units
 };
 
-// Exclusive prefix sum of a[0 .. n) in place (n <= 4 * PLAN_THREADS); returns the total.  All threads call it.
+// Exclusive prefix sum of a[0 .. n) in place; returns the total.  All threads call it.
 __device__ int block_exclusive_scan(int* a, int n, int* chunk) {
   const int tid = threadIdx.x;
   const int per = (n + PLAN_THREADS - 1) / PLAN_THREADS;
@@ -513,16 +566,16 @@ __device__ int block_exclusive_scan(int* a, int n, int* chunk) {
 __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(PrefillKernelArgs p, PlanArgs pa) {
   __shared__ int uoff[PLAN_MAX_BATCH + 1];  // first unit of each sequence
   __shared__ int sc0[PLAN_MAX_BATCH], snk[PLAN_MAX_BATCH];
-  __shared__ int start[PLAN_BUCKETS];       // bucket i holds units with PLAN_BUCKETS - i key tiles (clamped)
+  __shared__ int start[PLAN_BUCKETS];       // bucket i holds units with `buckets` - i key tiles (clamped)
   __shared__ int chunk[PLAN_THREADS];
-  const int tid = threadIdx.x, nb = pa.batch;
+  const int tid = threadIdx.x, nb = pa.batch, nbk = pa.buckets;
   for (int b = tid; b < nb; b += PLAN_THREADS) {
     const SeqGeom g = seq_geom(p, b);
     uoff[b] = min(g.T, p.max_tiles);  // rows past max_seqlen_q are not computed
     sc0[b] = g.c0;
     snk[b] = g.NKe;
   }
-  for (int i = tid; i < PLAN_BUCKETS; i += PLAN_THREADS) start[i] = 0;
+  for (int i = tid; i < nbk; i += PLAN_THREADS) start[i] = 0;
   __syncthreads();
   const int units = min(block_exclusive_scan(uoff, nb, chunk), pa.unit_cap);
   if (tid == 0) uoff[nb] = units;
@@ -537,14 +590,14 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(PrefillKerne
     b = lo;
     t = u - uoff[lo];
     const int nk = min(max(t + 1 + sc0[lo], 1), snk[lo]);
-    return PLAN_BUCKETS - min(nk, PLAN_BUCKETS);
+    return nbk - min(nk, nbk);
   };
   for (int u = tid; u < units; u += PLAN_THREADS) {
     int b, t;
     atomicAdd(&start[locate(u, b, t)], 1);
   }
   __syncthreads();
-  block_exclusive_scan(start, PLAN_BUCKETS, chunk);
+  block_exclusive_scan(start, nbk, chunk);
   for (int u = tid; u < units; u += PLAN_THREADS) {
     int b, t;
     const int slot = atomicAdd(&start[locate(u, b, t)], 1);
@@ -627,10 +680,16 @@ size_t prefill_workspace_bytes(int batch, int num_q_tokens, int max_seqlen_q, in
   return PLAN_HEADER_BYTES + size_t(cap) * sizeof(int2);
 }
 
-bool prefill_wants_order(const AttnArgs& a, int max_seqlen_k) {
-  // Causal self-attention over this step's own tokens: a query tile's work grows with its index, so the
-  // grid's latest-tile-first launch order already is longest-first.
-  return a.block_tables != nullptr || !a.causal || max_seqlen_k != a.max_seqlen_q;
+bool prefill_wants_order(const AttnArgs& a) {
+  // Cached prefixes of different lengths or non-causal rows: a query tile's work is not given by its index.
+  if (a.block_tables != nullptr || !a.causal || a.max_seqlen_k != a.max_seqlen_q) return true;
+  // Causal self-attention over this step's own tokens: a tile's work grows with its index, so the grid's
+  // latest-tile-first launch order already is longest-first -- but the grid holds batch x ceil(max_seqlen_q /
+  // 64) work-groups per kv head, and when the lengths vary enough that a tenth of them would find no tile
+  // (they still cost a dispatch each), the listed order is worth its planner.
+  const int64_t grid_tiles = int64_t(a.batch) * ((int64_t(a.max_seqlen_q) + BM - 1) / BM);
+  const int64_t real_tiles_max = (int64_t(a.num_q_tokens) + BM - 1) / BM + a.batch;
+  return real_tiles_max * 10 < grid_tiles * 9;
 }
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -664,6 +723,7 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, void* workspace, size_t worksp
   const size_t need = prefill_workspace_bytes(a.batch, a.num_q_tokens, a.max_seqlen_q, a.num_kv_heads);
   if (workspace && need > 0 && workspace_bytes >= need) {
     plan.batch = a.batch;
+    plan.buckets = int(std::min<int64_t>(PLAN_BUCKETS, (int64_t(std::max(a.max_seqlen_k, 0)) + BN - 1) / BN + 1));
     plan.unit_cap = int(unit_cap(a.batch, a.num_q_tokens, a.max_seqlen_q));
     plan.count = static_cast<int*>(workspace);
     plan.list = reinterpret_cast<int2*>(static_cast<char*>(workspace) + PLAN_HEADER_BYTES);

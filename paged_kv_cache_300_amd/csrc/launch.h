@@ -25,7 +25,7 @@ struct AttnArgs {
   const int32_t* block_tables; int max_blocks; int block_size;
   int64_t num_k_rows;  // contiguous rows, or slots of the paged cache
   int num_blocks;      // paged mode
-  int batch; int max_seqlen_q; int num_q_tokens;
+  int batch; int max_seqlen_q; int max_seqlen_k; int num_q_tokens;
   int num_q_heads; int num_kv_heads; int head_dim;
   float scale; int causal;
   void* out;
@@ -50,7 +50,7 @@ bool prefill_fast_strides_ok(int64_t k_stride, int64_t v_stride);
 // Workspace of the longest-first planner (0: not available for these sizes).
 size_t prefill_workspace_bytes(int batch, int num_q_tokens, int max_seqlen_q, int num_kv_heads);
 // Whether the longest-first order can beat the grid's launch order for this call.
-bool prefill_wants_order(const AttnArgs& a, int max_seqlen_k);
+bool prefill_wants_order(const AttnArgs& a);
 // workspace == NULL: grid order; else the planner orders the query tiles longest first.
 hipError_t launch_prefill_bf16(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
