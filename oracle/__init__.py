@@ -14,7 +14,8 @@ Sources (three web pages on the attention layer of nano-vLLM; cited by tag, page
 * [P1] "Nano-VLLM全代码解析笔记(5)-laynorm和attention", m.demingchina.com/news/18656
   -- the attention.py walkthrough and its questions Q1-Q6.
 * [P2] nano-vllm lesson on the Qwen3 attention sub-layer, www.yeyulingfeng.com/a/738130.html
-  -- §3 (GQA), §5.1 (store_kvcache), §5.2 (FlashAttention / online softmax), §5.3 (prefill / decode calls).
+  -- §2 (the seven steps), §3 (GQA), §4 (QK-Norm and RoPE), §5.1 (store_kvcache), §5.2 (FlashAttention /
+  online softmax), §5.3 (prefill / decode calls).
 * [P3] "课程 04 · KV 到底写到了哪一格", diomchen.github.io/lessons/0004-attention-slot-mapping.html
   -- §1 (the five tensors), §2 (slot_mapping), §3 (the scatter kernel), §4 (the two attention calls),
   §7 (exercise A), §9 (exercise C).
@@ -28,6 +29,7 @@ reading, stated in ``attention.kv_head_of``.
 from .bf16 import bf16_bits_to_f64, as_f64
 from .slots import slot_mapping_block_walk, slot_mapping_ref, decode_slot_ref
 from .store import store_ref, scatter_rows_ref
+from .qknorm_rope import rms_norm_ref, rope_ref, qk_norm_rope_ref
 from .attention import (
     kv_head_of,
     attention_ref,
@@ -45,6 +47,9 @@ __all__ = [
     "decode_slot_ref",
     "store_ref",
     "scatter_rows_ref",
+    "rms_norm_ref",
+    "rope_ref",
+    "qk_norm_rope_ref",
     "kv_head_of",
     "attention_ref",
     "decode_ref",
