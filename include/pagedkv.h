@@ -93,6 +93,28 @@ int kv_store(const void* key, int64_t key_stride, const void* value, int64_t val
              int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype, hipStream_t stream);
 
 /*
+ * kv_store_qk_norm_rope -- the steps between the qkv split and the attention call, fused: QK-Norm,
+ * RoPE, and the store of k and v [P2 §2 steps 4-6; §4; §5.1; P1 layernorm.py walkthrough].
+ *
+ * For token i (position positions[i]) and every head: q and k are divided by the root of their mean
+ * square over head_dim plus eps and multiplied elementwise by q_norm_weight / k_norm_weight
+ * ([head_dim] each, same dtype as q); then element e < head_dim/2 and element e + head_dim/2 of q and of k
+ * are rotated by the angle positions[i] * rope_theta^(-2e/head_dim) (the rotate-half rotary embedding);
+ * v is not changed.  The rotated k and the v row are written to cache slot slot_mapping[i] exactly as
+ * kv_store does (slot < 0 or >= num_slots skips the cache); the normalised, rotated q is written to q_out.
+ * q, k, v: [num_tokens, heads, head_dim] with token strides (rows of a merged qkv projection work as
+ * they are).  q_out: [num_tokens, num_q_heads, head_dim], contiguous.  head_dim: 16, 32, 64, 128 or 256.
+ * Arithmetic in float32 with one rounding to the storage type at the end; the angles are formed in
+ * float64 and reduced modulo 2 pi before the float32 sine and cosine.
+ */
+int kv_store_qk_norm_rope(const void* q, int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                          int64_t v_stride, const int32_t* positions, const void* q_norm_weight,
+                          const void* k_norm_weight, float eps, float rope_theta, void* q_out, void* k_cache,
+                          void* v_cache, int64_t num_slots, const int32_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                          hipStream_t stream);
+
+/*
  * attn_prefill_varlen -- varlen attention for a prefill step [P2 §5.3; P3 §4; P1 Q6 §3].
  *
  * Sequence b has query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q (token stride q_stride) and

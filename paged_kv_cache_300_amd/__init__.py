@@ -20,6 +20,7 @@ from ._lib import (
     library_path,
     kv_slot_mapping,
     kv_store,
+    kv_store_qk_norm_rope,
     attn_prefill_varlen,
     attn_prefill_workspace_bytes,
     attn_decode_workspace_bytes,
@@ -34,6 +35,7 @@ __all__ = [
     "library_path",
     "kv_slot_mapping",
     "kv_store",
+    "kv_store_qk_norm_rope",
     "attn_prefill_varlen",
     "attn_prefill_workspace_bytes",
     "attn_decode_workspace_bytes",

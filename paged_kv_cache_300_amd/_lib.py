@@ -42,6 +42,9 @@ def lib():
     L.kv_slot_mapping.restype = ctypes.c_int
     L.kv_store.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i32, i32, i32, ctypes.c_int, vp]
     L.kv_store.restype = ctypes.c_int
+    L.kv_store_qk_norm_rope.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, vp, i64, vp, i32,
+                                        i32, i32, i32, ctypes.c_int, vp]
+    L.kv_store_qk_norm_rope.restype = ctypes.c_int
     L.attn_prefill_varlen.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i32, i32, i64, i32, i32, i32,
                                       f32, i32, vp, i32, i32, vp, vp, sz, ctypes.c_int, vp]
     L.attn_prefill_varlen.restype = ctypes.c_int
@@ -150,6 +153,48 @@ def kv_store(key, value, k_cache, v_cache, slot_mapping):
     rc = lib().kv_store(_ptr(key), ks, _ptr(value), vs, _ptr(k_cache), _ptr(v_cache), num_slots, _ptr(slot_mapping),
                         n, hkv, hd, _dtype_code(key), _stream(key))
     _check("kv_store", rc)
+
+
+def kv_store_qk_norm_rope(q, k, v, positions, q_norm_weight, k_norm_weight, k_cache, v_cache, slot_mapping,
+                          eps=1e-6, rope_theta=1e6, q_out=None):
+    """QK-Norm and RoPE of the new tokens' q and k, then store_kvcache of k and v (one fused pass).
+
+    q: [N, Hq, hd], k and v: [N, Hkv, hd] (rows may come from a merged qkv projection), positions: [N] int32
+    absolute positions, q_norm_weight / k_norm_weight: [hd].  Returns q_out [N, Hq, hd], normalised and
+    rotated; k (normalised, rotated) and v go to the caches at slot_mapping (slot < 0 skipped).
+    """
+    _dev(q, "q"); _dev(k, "k"); _dev(v, "v")
+    _cache(k_cache, "k_cache"); _cache(v_cache, "v_cache")
+    _meta(positions, "positions"); _meta(slot_mapping, "slot_mapping")
+    n, hq, hd = q.shape
+    qs = _rows(q, "q")
+    ks = _rows(k, "k")
+    hkv = k.shape[1]
+    vs = _rows(v, "v", hkv)
+    if k.shape != (n, hkv, hd) or v.shape != k.shape:
+        raise ValueError("k and v must be [N, Hkv, head_dim] with q's N and head_dim")
+    if k_cache.shape != v_cache.shape or k_cache.shape[2:] != (hkv, hd):
+        raise ValueError("caches must be [num_blocks, block_size, Hkv, head_dim]")
+    if positions.numel() != n or slot_mapping.numel() != n:
+        raise ValueError("positions and slot_mapping need one entry per token")
+    for w, name in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        _dev(w, name)
+        if w.shape != (hd,) or not w.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [head_dim] tensor")
+    if not (q.dtype == k.dtype == v.dtype == k_cache.dtype == v_cache.dtype == q_norm_weight.dtype ==
+            k_norm_weight.dtype):
+        raise ValueError("q, k, v, the caches and the norm weights must share a dtype")
+    if q_out is None:
+        q_out = torch.empty((n, hq, hd), dtype=q.dtype, device=q.device)
+    elif q_out.shape != (n, hq, hd) or not q_out.is_contiguous() or q_out.dtype != q.dtype:
+        raise ValueError("q_out must be a contiguous [N, Hq, head_dim] tensor of q's dtype")
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    rc = lib().kv_store_qk_norm_rope(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _ptr(positions), _ptr(q_norm_weight),
+                                     _ptr(k_norm_weight), float(eps), float(rope_theta), _ptr(q_out), _ptr(k_cache),
+                                     _ptr(v_cache), num_slots, _ptr(slot_mapping), n, hq, hkv, hd, _dtype_code(q),
+                                     _stream(q))
+    _check("kv_store_qk_norm_rope", rc)
+    return q_out
 
 
 def attn_prefill_workspace_bytes(batch, num_q_tokens, max_seqlen_q, num_q_heads, num_kv_heads, head_dim,

@@ -17,7 +17,8 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["abi.cpp", "slot_store.hip", "attn_generic.hip", "attn_decode.hip", "attn_prefill.hip"]
+SOURCES = ["abi.cpp", "slot_store.hip", "qknorm_rope_store.hip", "attn_generic.hip", "attn_decode.hip",
+           "attn_prefill.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

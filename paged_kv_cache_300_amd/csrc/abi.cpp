@@ -98,6 +98,34 @@ int kv_store(const void* key, int64_t key_stride, const void* value, int64_t val
                     "kv_store launch");
 }
 
+int kv_store_qk_norm_rope(const void* q, int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                          int64_t v_stride, const int32_t* positions, const void* q_norm_weight,
+                          const void* k_norm_weight, float eps, float rope_theta, void* q_out, void* k_cache,
+                          void* v_cache, int64_t num_slots, const int32_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                          hipStream_t stream) {
+  g_error.clear();
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
+  if (!pkv::qknorm_rope_supported(head_dim))
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: 16, 32, 64, 128 or 256 are supported", head_dim);
+  if (num_tokens < 0 || num_slots < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens and num_slots must be >= 0");
+  if (q_stride < int64_t(num_q_heads) * head_dim || k_stride < int64_t(num_kv_heads) * head_dim ||
+      v_stride < int64_t(num_kv_heads) * head_dim)
+    return fail(PKV_ERR_INVALID_ARG, "token strides must cover a row of heads * head_dim elements");
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(PKV_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!(rope_theta > 0.f) || !isfinite(rope_theta)) return fail(PKV_ERR_INVALID_ARG, "rope_theta must be > 0");
+  if (num_tokens == 0) return PKV_OK;
+  if (!q || !k || !v || !positions || !q_norm_weight || !k_norm_weight || !q_out || !k_cache || !v_cache ||
+      !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "every pointer must be non-null");
+  return hip_status(pkv::launch_qknorm_rope_store(q, q_stride, k, k_stride, v, v_stride, positions, q_norm_weight,
+                                                  k_norm_weight, eps, rope_theta, q_out, k_cache, v_cache,
+                                                  num_slots, slot_mapping, num_tokens, num_q_heads,
+                                                  num_kv_heads, head_dim, dtype == PKV_BF16, stream),
+                    "kv_store_qk_norm_rope launch");
+}
+
 int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t k_stride, const void* v,
                         int64_t v_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                         int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t batch, int32_t num_q_tokens,

@@ -16,6 +16,16 @@ hipError_t launch_kv_store(const void* key, int64_t key_stride, const void* valu
                            void* k_cache, void* v_cache, int64_t num_slots, const int32_t* slot_mapping,
                            int num_tokens, int row_elems, int elem_bytes, hipStream_t stream);
 
+// QK-Norm + RoPE of q and k, then the store of k and v (head_dim 16 .. 256, powers of two).
+bool qknorm_rope_supported(int head_dim);
+hipError_t launch_qknorm_rope_store(const void* q, int64_t q_stride, const void* k, int64_t k_stride,
+                                    const void* v, int64_t v_stride, const int32_t* positions,
+                                    const void* q_norm_weight, const void* k_norm_weight, float eps,
+                                    float rope_theta, void* q_out, void* k_cache, void* v_cache,
+                                    int64_t num_slots, const int32_t* slot_mapping, int num_tokens,
+                                    int num_q_heads, int num_kv_heads, int head_dim, bool bf16,
+                                    hipStream_t stream);
+
 // Any dtype, head_dim <= 256, any block size; prefill (cu_q != NULL) or decode (ctx_lens != NULL).
 struct AttnArgs {
   const void* q; int64_t q_stride;

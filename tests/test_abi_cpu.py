@@ -27,7 +27,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for fn in ("kv_slot_mapping", "kv_store", "attn_prefill_varlen", "attn_prefill_workspace_bytes",
+    for fn in ("kv_slot_mapping", "kv_store", "kv_store_qk_norm_rope", "attn_prefill_varlen",
+               "attn_prefill_workspace_bytes",
                "attn_decode_paged", "attn_decode_workspace_bytes", "pkv_last_error"):
         assert fn in names
 
@@ -58,6 +59,18 @@ def test_store_rejects_bad_arguments_on_host():
     # nothing to do is fine and launches nothing
     assert L.kv_store(None, 8, None, 8, None, None, 0, None, 0, 1, 8, pkv.PKV_F32, None) == 0
     assert _err(L) == ""
+
+
+def test_qk_norm_rope_store_rejects_bad_arguments_on_host():
+    pkv, L = _lib()
+    fake = ctypes.c_void_p(0x1000)
+    args = lambda hd, eps, theta, qs: (fake, qs, fake, 8 * hd, fake, 8 * hd, fake, fake, fake, eps, theta, fake, fake,
+                                       fake, 4096, fake, 4, 16, 8, hd, pkv.PKV_BF16, None)
+    assert L.kv_store_qk_norm_rope(*args(96, 1e-6, 1e6, 16 * 96)) == -2          # head_dim not a power of two
+    assert L.kv_store_qk_norm_rope(*args(128, -1.0, 1e6, 16 * 128)) == -1        # negative eps
+    assert L.kv_store_qk_norm_rope(*args(128, 1e-6, 0.0, 16 * 128)) == -1        # theta must be > 0
+    assert L.kv_store_qk_norm_rope(*args(128, 1e-6, 1e6, 15 * 128)) == -1        # q stride shorter than a row
+    assert "stride" in _err(L)
 
 
 def test_slot_mapping_rejects_bad_arguments_on_host():
