@@ -222,6 +222,40 @@ def bench_store(pkv, torch, steps, warmup):
     return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n}
 
 
+def bench_qknorm_rope_store(pkv, torch, make, steps, warmup, layers):
+    """The fused QK-Norm + RoPE + store over one prefill step's new tokens (workload 3's q, k, v)."""
+    cases, _ = dev_case_layers(make, layers, torch)
+    c0 = cases[0]
+    n, hq, hkv, hd = int(c0.cu_seqlens_q[-1]), c0.num_q_heads, c0.num_kv_heads, c0.head_dim
+    bt = torch.from_numpy(c0.block_tables).cuda()
+    cu_q = torch.from_numpy(c0.cu_seqlens_q).cuda()
+    cu_k = torch.from_numpy(c0.cu_seqlens_k).cuda()
+    sm = pkv.kv_slot_mapping(bt, c0.block_size, n, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+    pos = torch.cat([torch.arange(int(lk) - int(lq), int(lk), dtype=torch.int32) for lq, lk in zip(c0.Lq, c0.Lk)])
+    pos = pos.cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    wq = (1 + 0.1 * torch.randn(hd, generator=gen, device="cuda")).to(torch.bfloat16)
+    wk = (1 + 0.1 * torch.randn(hd, generator=gen, device="cuda")).to(torch.bfloat16)
+    shape = (c0.num_blocks, c0.block_size, hkv, hd)
+    caches = [(torch.zeros(shape, dtype=torch.bfloat16, device="cuda"),
+               torch.zeros(shape, dtype=torch.bfloat16, device="cuda")) for _ in cases]
+    outs = [torch.empty_like(c.q) for c in cases]
+    torch.cuda.synchronize()
+
+    def step(i):
+        L = i % layers
+        c, (kc, vc) = cases[L], caches[L]
+        pkv.kv_store_qk_norm_rope(c.q, c.k, c.v, pos, wq, wk, kc, vc, sm, q_out=outs[L])
+
+    wall_ms = run_steps(torch, step, steps, warmup)
+    kern_ms = time_kernel(torch, step, steps)
+    moved = 2 * n * (hq + 2 * hkv) * hd * 2 + 8 * n  # q, k, v read and written once, plus positions and slots
+    del caches, cases
+    torch.cuda.empty_cache()
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n}
+
+
 # ------------------------------------------------------------------------------------------------ CPU side
 
 def cpu_baseline(min_seconds=10.0, n_seqs=16):
@@ -269,7 +303,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode"], default=None,
+    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope"], default=None,
                     help="run just one secondary workload (after the headline), e.g. for a profiler")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -298,7 +332,7 @@ def main():
     secondary = {}
     if not args.headline_only:
         want = lambda name: args.only in (None, name)
-        p3 = p4 = st = d5 = None
+        p3 = p4 = st = d5 = qr = None
         if want("prefill"):
             log("prefill, workload 3")
             p3 = bench_prefill(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers, paged=False)
@@ -308,6 +342,9 @@ def main():
         if want("store"):
             log("store sweep, workload 5")
             st = bench_store(pkv, torch, args.steps, args.warmup)
+        if want("qknorm_rope"):
+            log("QK-Norm + RoPE + store, workload 3's tokens")
+            qr = bench_qknorm_rope_store(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers)
         if want("long_decode"):
             log("long padded decode, workload 5")
             d5 = bench_decode(pkv, torch, workloads.workload5_decode, max(args.steps // 5, 3), 2, 2)
@@ -324,6 +361,12 @@ def main():
                                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                                  "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
                                                  "tokens": st["tokens"]}
+        if qr is not None:
+            gbq = qr["bytes"] / (qr["kernel_ms"] * 1e-3) / 1e9
+            secondary["qknorm_rope_store_workload3"] = {"value": round(gbq, 1), "unit": "GB/s",
+                                                       "frac_hbm_peak": round(gbq / HBM_PEAK_GBS, 4),
+                                                       "kernel_ms": round(qr["kernel_ms"], 5), "bytes": qr["bytes"],
+                                                       "tokens": qr["tokens"]}
         if d5 is not None:
             gbs5 = d5["kv_bytes"] / (d5["kernel_ms"] * 1e-3) / 1e9
             secondary["long_decode_workload5"] = {"value": round(gbs5, 1), "unit": "GB/s",

@@ -72,6 +72,10 @@ def _check(pkv, case, positions, sm, *, eps=1e-6, theta=1e6, seed=0, q=None, k=N
     ("bf16", 4, 2, 32, [17], [100], 8, 104),
     ("f32", 4, 2, 16, [6, 3], [0, 0], 4, 105),   # the tiny fp32 layer's shape
     ("f32", 16, 8, 128, [50], [20], 256, 106),
+    ("bf16", 6, 3, 128, [45, 2], [7, 0], 16, 111),   # 12 rows a token: a short last chunk of rows
+    ("bf16", 4, 2, 16, [300], [0], 32, 112),          # two lanes a row
+    ("f32", 32, 8, 256, [20, 5], [0, 9], 16, 113),    # 48 rows a token: more chunks than lane groups
+    ("f32", 6, 3, 64, [31], [2], 8, 114),
 ])
 def test_prefill_tokens(pkv, dtype, hq, hkv, hd, lq, prefix, bs, seed):
     lk = [a + b for a, b in zip(lq, prefix)]
@@ -117,3 +121,22 @@ def test_rows_of_a_merged_qkv_projection(pkv):
     sm = oracle.slot_mapping_ref(case.block_tables, 256, n, cu_seqlens_q=case.cu_seqlens_q,
                                  cu_seqlens_k=case.cu_seqlens_k)
     _check(pkv, case, _positions(case), sm, seed=110, q=q, k=k, v=v)
+
+
+def test_unaligned_rows_take_the_elementwise_kernel(pkv):
+    """q, k and v starting 2 bytes past a 16-byte boundary: the element-wise kernel, same results."""
+    case = workloads.make_case([37, 12], [40, 12], num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=16,
+                               num_blocks=8, dtype="bf16", seed=115)
+    n = 49
+
+    def shifted(x, heads):
+        buf = torch.empty(n * heads * 128 + 1, dtype=torch.bfloat16, device="cuda")
+        view = buf[1:].view(n, heads, 128)
+        view.copy_(to_dev(x, "bf16"))
+        assert view.data_ptr() % 16 == 2
+        return view
+
+    sm = oracle.slot_mapping_ref(case.block_tables, 16, n, cu_seqlens_q=case.cu_seqlens_q,
+                                 cu_seqlens_k=case.cu_seqlens_k)
+    _check(pkv, case, _positions(case), sm, seed=115, q=shifted(case.q, 16), k=shifted(case.k, 8),
+           v=shifted(case.v, 8))
