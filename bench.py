@@ -121,7 +121,7 @@ def build_caches(pkv, torch, case):
     return kc, vc
 
 
-def bench_decode(pkv, torch, make, steps, warmup, layers):
+def bench_decode(pkv, torch, make, steps, warmup, layers, fused=False):
     cases, _ = dev_case_layers(make, layers, torch)
     c0 = cases[0]
     meta = {
@@ -145,12 +145,20 @@ def bench_decode(pkv, torch, make, steps, warmup, layers):
         c, (kc, vc) = cases[L], caches[L]
         pkv.attn_decode_paged(c.q, kc, vc, meta["ctx"], meta["bt"], c0.scale, out=outs[L], workspace=ws)
 
+    def fused_step(L):
+        c, (kc, vc) = cases[L], caches[L]
+        pkv.attn_decode_paged_store(c.q, c.k, c.v, kc, vc, meta["ctx"], meta["bt"], c0.scale, out=outs[L],
+                                    workspace=ws, slot_mapping_out=sm)
+
     def step(i):
-        store(i % layers)
-        attend(i % layers)
+        if fused:
+            fused_step(i % layers)
+        else:
+            store(i % layers)
+            attend(i % layers)
 
     wall_ms = run_steps(torch, step, steps, warmup)
-    kern_ms = time_kernel(torch, lambda i: attend(i % layers), steps)
+    kern_ms = time_kernel(torch, lambda i: (fused_step if fused else attend)(i % layers), steps)
     kv_bytes = int(c0.Lk.astype(int).sum()) * 2 * c0.num_kv_heads * c0.head_dim * 2
     del caches, cases
     torch.cuda.empty_cache()
@@ -303,7 +311,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope"], default=None,
+    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope", "fused_decode"],
+                    default=None,
                     help="run just one secondary workload (after the headline), e.g. for a profiler")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -332,7 +341,10 @@ def main():
     secondary = {}
     if not args.headline_only:
         want = lambda name: args.only in (None, name)
-        p3 = p4 = st = d5 = qr = None
+        p3 = p4 = st = d5 = qr = fd = None
+        if want("fused_decode"):
+            log("fused store + decode step, workload 2")
+            fd = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers, fused=True)
         if want("prefill"):
             log("prefill, workload 3")
             p3 = bench_prefill(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers, paged=False)
@@ -361,6 +373,12 @@ def main():
                                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                                  "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
                                                  "tokens": st["tokens"]}
+        if fd is not None:
+            secondary["decode_step_fused_workload2"] = {
+                "value": round(fd["kv_bytes"] / (fd["wall_ms"] * 1e-3) / 1e9, 1), "unit": "GB/s",
+                "step_ms": round(fd["wall_ms"], 5), "kernel_ms": round(fd["kernel_ms"], 5),
+                "kernel_GBps": round(fd["kv_bytes"] / (fd["kernel_ms"] * 1e-3) / 1e9, 1),
+                "step": "attn_decode_paged_store (slot_mapping + store + decode in one call)"}
         if qr is not None:
             gbq = qr["bytes"] / (qr["kernel_ms"] * 1e-3) / 1e9
             secondary["qknorm_rope_store_workload3"] = {"value": round(gbq, 1), "unit": "GB/s",

@@ -3,9 +3,11 @@
  *
  * One attention layer of a GQA decoder step, as three operations on one GPU:
  *   kv_store             scatter each new token's K/V row into a paged cache by slot_mapping;
+ *   kv_store_qk_norm_rope  the same store with QK-Norm and RoPE of q and k fused in front of it;
  *   attn_prefill_varlen  causal attention over sequences packed by cu_seqlens, reading K/V either from
  *                        this step's rows or, for prefix-cache / chunked prefill, from the paged cache;
  *   attn_decode_paged    one query per sequence against its whole history in the paged cache;
+ *   attn_decode_paged_store  the decode step's store and attention fused in one call;
  * plus kv_slot_mapping, which builds slot_mapping from the block tables on the device.
  *
  * Sources (three web pages on the attention layer of nano-vLLM; cited by tag, title and section):
@@ -182,6 +184,31 @@ int attn_decode_paged(const void* q, int64_t q_stride, const void* k_cache, cons
                       int32_t batch, int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, float softmax_scale, void* out,
                       void* workspace, size_t workspace_bytes, pkv_dtype dtype, hipStream_t stream);
+
+/*
+ * attn_decode_paged_store -- the decode step's store and its attention in one call: store_kvcache of each
+ * row's new token [P2 §5.1; P3 §3], then attn_decode_paged over the cache that includes it [P2 §5.3; P3 §4
+ * note on the order], with the slot computed from the block table [P3 §9 exercise C].
+ *
+ * Results equal kv_slot_mapping(context_lens mode) + kv_store + attn_decode_paged on the same arguments, bit
+ * for bit (output and cache).  Row b's new token sits at position context_lens[b] - 1; its K and V rows
+ * (k_new, v_new: [batch, num_kv_heads, head_dim], token strides k_new_stride / v_new_stride in elements) are
+ * written to slot block_tables[b][p / block_size] * block_size + p % block_size and attended as key p.  Rows
+ * with context_lens[b] <= 0, a position past the table, or a block-table entry outside [0, num_blocks) write
+ * nothing (padding rows give a zero output).  With bf16 and head_dim 128 the store happens inside the decode
+ * kernel (the new rows are read once, from k_new / v_new, and written from registers); other shapes launch a
+ * store kernel, then the decode.
+ * slot_mapping_out: NULL, or [batch] int32 receiving the same slots as kv_slot_mapping (-1: none).
+ * Other arguments, workspace (attn_decode_workspace_bytes) and errors: as attn_decode_paged.  The caches must
+ * not overlap k_new / v_new.  Limits: num_blocks * block_size < 2^31.
+ */
+int attn_decode_paged_store(const void* q, int64_t q_stride, const void* k_new, int64_t k_new_stride,
+                            const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache,
+                            int32_t num_blocks, const int32_t* context_lens, const int32_t* block_tables,
+                            int32_t batch, int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, float softmax_scale, void* out,
+                            int32_t* slot_mapping_out, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

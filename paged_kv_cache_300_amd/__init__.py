@@ -25,6 +25,7 @@ from ._lib import (
     attn_prefill_workspace_bytes,
     attn_decode_workspace_bytes,
     attn_decode_paged,
+    attn_decode_paged_store,
 )
 
 __all__ = [
@@ -40,4 +41,5 @@ __all__ = [
     "attn_prefill_workspace_bytes",
     "attn_decode_workspace_bytes",
     "attn_decode_paged",
+    "attn_decode_paged_store",
 ]

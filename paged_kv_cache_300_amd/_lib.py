@@ -55,6 +55,9 @@ def lib():
     L.attn_decode_paged.argtypes = [vp, i64, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, sz,
                                     ctypes.c_int, vp]
     L.attn_decode_paged.restype = ctypes.c_int
+    L.attn_decode_paged_store.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                          i32, f32, vp, vp, vp, sz, ctypes.c_int, vp]
+    L.attn_decode_paged_store.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -294,4 +297,49 @@ def attn_decode_paged(q, k_cache, v_cache, cache_seqlens, block_table, softmax_s
                                  _ptr(block_table), b, max_blocks, bs, hq, hkv, hd, float(softmax_scale), _ptr(out),
                                  _ptr(workspace), ws_bytes, _dtype_code(q), _stream(q))
     _check("attn_decode_paged", rc)
+    return out
+
+
+def attn_decode_paged_store(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, softmax_scale, out=None,
+                            workspace=None, slot_mapping_out=None):
+    """The decode step in one call: each row's new k/v ([B, Hkv, hd]) to its slot (position cache_seqlens[b] - 1
+    through block_table), then attention over the cache including it; returns [B, Hq, hd].  Same results as
+    kv_slot_mapping + kv_store + attn_decode_paged.  ``slot_mapping_out`` ([B] int32) receives the slots."""
+    _dev(q, "q")
+    if q.dim() == 4 and q.shape[1] == 1:
+        q = q[:, 0]
+    _cache(k_cache, "k_cache"); _cache(v_cache, "v_cache")
+    _meta(cache_seqlens, "cache_seqlens"); _meta(block_table, "block_table")
+    b, hq, hd = q.shape
+    qs = _rows(q, "q")
+    num_blocks, bs, hkv, hd_c = k_cache.shape
+    if k_cache.shape != v_cache.shape or hd_c != hd:
+        raise ValueError("caches must match each other and q's head_dim")
+    _dev(k_new, "k_new"); _dev(v_new, "v_new")
+    ks = _rows(k_new, "k_new", hkv)
+    vs = _rows(v_new, "v_new", hkv)
+    if k_new.shape != (b, hkv, hd) or v_new.shape != (b, hkv, hd):
+        raise ValueError("k_new and v_new must be [B, Hkv, head_dim]")
+    if not (q.dtype == k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_new, v_new and the caches must share a dtype")
+    if cache_seqlens.numel() != b or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("cache_seqlens [B] and block_table [B, max_blocks] must match q's batch")
+    if slot_mapping_out is not None:
+        _meta(slot_mapping_out, "slot_mapping_out")
+        if slot_mapping_out.numel() != b:
+            raise ValueError("slot_mapping_out must have one entry per row")
+    max_blocks = block_table.shape[1]
+    need = attn_decode_workspace_bytes(b, hq, hkv, hd, max_blocks, bs, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((b, hq, hd), dtype=q.dtype, device=q.device)
+    elif out.shape != (b, hq, hd) or not out.is_contiguous() or out.dtype != q.dtype:
+        raise ValueError("out must be a contiguous [B, Hq, head_dim] tensor of q's dtype")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().attn_decode_paged_store(_ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(k_cache), _ptr(v_cache),
+                                       num_blocks, _ptr(cache_seqlens), _ptr(block_table), b, max_blocks, bs, hq, hkv,
+                                       hd, float(softmax_scale), _ptr(out), _ptr(slot_mapping_out), _ptr(workspace),
+                                       ws_bytes, _dtype_code(q), _stream(q))
+    _check("attn_decode_paged_store", rc)
     return out

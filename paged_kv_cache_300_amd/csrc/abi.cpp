@@ -45,6 +45,66 @@ int check_heads(int32_t hq, int32_t hkv, int32_t hd) {
   return PKV_OK;
 }
 
+// attn_decode_paged and attn_decode_paged_store share their checks and dispatch; fused != NULL also stores each
+// row's new token (fast path: inside the decode kernel; other shapes: a store kernel, then the decode).
+int decode_call(const char* name, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                int32_t num_blocks, const int32_t* context_lens, const int32_t* block_tables, int32_t batch,
+                int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                int32_t head_dim, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                pkv_dtype dtype, hipStream_t stream, const pkv::DecodeStoreArgs* fused) {
+  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+  if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
+  if (batch < 0 || num_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "batch and num_blocks must be >= 0");
+  if (batch > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "batch %d too large", batch);
+  if (block_size < 1 || max_blocks_per_seq < 1)
+    return fail(PKV_ERR_INVALID_ARG, "block_size and max_blocks_per_seq must be >= 1");
+  if (int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "contexts beyond 2^31 tokens are not supported");
+  if (fused && int64_t(num_blocks) * block_size > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "caches beyond 2^31 slots are not supported by the int32 slot_mapping");
+  if (!isfinite(softmax_scale)) return fail(PKV_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (q_stride < int64_t(num_q_heads) * head_dim)
+    return fail(PKV_ERR_INVALID_ARG, "q_stride must be >= num_q_heads*head_dim");
+  const int64_t kv_row = int64_t(num_kv_heads) * head_dim;
+  if (fused && (fused->k_new_stride < kv_row || fused->v_new_stride < kv_row))
+    return fail(PKV_ERR_INVALID_ARG, "k_new_stride and v_new_stride must be >= num_kv_heads*head_dim");
+  if (batch == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !context_lens || !block_tables || !out)
+    return fail(PKV_ERR_INVALID_ARG, "q, caches, context_lens, block_tables and out must be non-null");
+  if (fused && (!fused->k_new || !fused->v_new)) return fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be non-null");
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  const bool bf16 = dtype == PKV_BF16;
+  pkv::AttnArgs a{};
+  a.q = q; a.q_stride = q_stride; a.k = k_cache; a.v = v_cache;
+  a.k_stride = a.v_stride = kv_row;
+  a.cu_q = nullptr; a.cu_k = nullptr; a.ctx_lens = context_lens;
+  a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq; a.block_size = block_size;
+  a.num_k_rows = int64_t(num_blocks) * block_size; a.num_blocks = num_blocks;
+  a.batch = batch; a.max_seqlen_q = 1; a.num_q_tokens = batch;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.scale = softmax_scale; a.causal = 1; a.out = out;
+  bool fast = pkv::decode_fast_supported(head_dim, num_q_heads / num_kv_heads, bf16) && aligned16(q) &&
+              q_stride % 8 == 0 && aligned16(k_cache) && aligned16(v_cache);
+  if (fast && fused)
+    fast = aligned16(fused->k_new) && aligned16(fused->v_new) && fused->k_new_stride % 8 == 0 &&
+           fused->v_new_stride % 8 == 0;
+  if (fast) {
+    const pkv::DecodePlan plan =
+        pkv::decode_plan(batch, num_q_heads, num_kv_heads, max_blocks_per_seq * block_size);
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace_bytes,
+                  workspace ? workspace_bytes : size_t(0));
+    return hip_status(pkv::launch_decode_bf16(a, plan, workspace, stream, fused), name);
+  }
+  if (fused) {
+    const hipError_t e = pkv::launch_decode_store(*fused, context_lens, block_tables, batch, max_blocks_per_seq,
+                                                  block_size, num_blocks, const_cast<void*>(k_cache),
+                                                  const_cast<void*>(v_cache), int(kv_row), bf16 ? 2 : 4, stream);
+    if (e != hipSuccess) return hip_status(e, name);
+  }
+  return hip_status(pkv::launch_attn_generic(a, bf16, stream), name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,42 +273,25 @@ int attn_decode_paged(const void* q, int64_t q_stride, const void* k_cache, cons
                       int32_t head_dim, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                       pkv_dtype dtype, hipStream_t stream) {
   g_error.clear();
-  if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
-  if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
-  if (batch < 0 || num_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "batch and num_blocks must be >= 0");
-  if (batch > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "batch %d too large", batch);
-  if (block_size < 1 || max_blocks_per_seq < 1)
-    return fail(PKV_ERR_INVALID_ARG, "block_size and max_blocks_per_seq must be >= 1");
-  if (int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
-    return fail(PKV_ERR_UNSUPPORTED, "contexts beyond 2^31 tokens are not supported");
-  if (!isfinite(softmax_scale)) return fail(PKV_ERR_INVALID_ARG, "softmax_scale must be finite");
-  if (q_stride < int64_t(num_q_heads) * head_dim)
-    return fail(PKV_ERR_INVALID_ARG, "q_stride must be >= num_q_heads*head_dim");
-  if (batch == 0) return PKV_OK;
-  if (!q || !k_cache || !v_cache || !context_lens || !block_tables || !out)
-    return fail(PKV_ERR_INVALID_ARG, "q, caches, context_lens, block_tables and out must be non-null");
-  if (num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
-  const bool bf16 = dtype == PKV_BF16;
-  pkv::AttnArgs a{};
-  a.q = q; a.q_stride = q_stride; a.k = k_cache; a.v = v_cache;
-  a.k_stride = a.v_stride = int64_t(num_kv_heads) * head_dim;
-  a.cu_q = nullptr; a.cu_k = nullptr; a.ctx_lens = context_lens;
-  a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq; a.block_size = block_size;
-  a.num_k_rows = int64_t(num_blocks) * block_size; a.num_blocks = num_blocks;
-  a.batch = batch; a.max_seqlen_q = 1; a.num_q_tokens = batch;
-  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
-  a.scale = softmax_scale; a.causal = 1; a.out = out;
-  const bool fast = pkv::decode_fast_supported(head_dim, num_q_heads / num_kv_heads, bf16) && aligned16(q) &&
-                    q_stride % 8 == 0 && aligned16(k_cache) && aligned16(v_cache);
-  if (fast) {
-    const pkv::DecodePlan plan =
-        pkv::decode_plan(batch, num_q_heads, num_kv_heads, max_blocks_per_seq * block_size);
-    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
-      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace_bytes,
-                  workspace ? workspace_bytes : size_t(0));
-    return hip_status(pkv::launch_decode_bf16(a, plan, workspace, stream), "attn_decode_paged launch");
-  }
-  return hip_status(pkv::launch_attn_generic(a, bf16, stream), "attn_decode_paged launch");
+  return decode_call("attn_decode_paged launch", q, q_stride, k_cache, v_cache, num_blocks, context_lens,
+                     block_tables, batch, max_blocks_per_seq, block_size, num_q_heads, num_kv_heads, head_dim,
+                     softmax_scale, out, workspace, workspace_bytes, dtype, stream, nullptr);
+}
+
+int attn_decode_paged_store(const void* q, int64_t q_stride, const void* k_new, int64_t k_new_stride,
+                            const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache, int32_t num_blocks,
+                            const int32_t* context_lens, const int32_t* block_tables, int32_t batch,
+                            int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, float softmax_scale, void* out,
+                            int32_t* slot_mapping_out, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                            hipStream_t stream) {
+  g_error.clear();
+  pkv::DecodeStoreArgs f;
+  f.k_new = k_new; f.k_new_stride = k_new_stride; f.v_new = v_new; f.v_new_stride = v_new_stride;
+  f.slot_out = slot_mapping_out;
+  return decode_call("attn_decode_paged_store launch", q, q_stride, k_cache, v_cache, num_blocks, context_lens,
+                     block_tables, batch, max_blocks_per_seq, block_size, num_q_heads, num_kv_heads, head_dim,
+                     softmax_scale, out, workspace, workspace_bytes, dtype, stream, &f);
 }
 
 }  // extern "C"

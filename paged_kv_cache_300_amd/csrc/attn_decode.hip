@@ -25,6 +25,12 @@
 //    range the 8 groups are merged with lane shuffles; a sequence wholly inside one range is written
 //    directly, otherwise each range writes (m, l, unnormalised output) and a combine kernel merges them with
 //    the same exact rescaling by exp(m_i - m).
+//  * Fused with the store (attn_decode_paged_store) [P2 §5.1 then §5.3; P3 §4 note on the order]: the new
+//    token of sequence b sits at position context_lens[b] - 1, the last key of b.  Only the worker whose key
+//    range ends b reads that slot, so that worker itself copies the token's K and V rows from the step's
+//    k_new / v_new rows into the slot (each wave its kv head's 512 bytes) and waits for the write before
+//    its first read of the sequence; no other work-group reads the slot and nothing else waits.  The first
+//    work-group can also write the step's slot_mapping.
 #include <math.h>
 
 #include <algorithm>
@@ -71,6 +77,13 @@ struct DecodeKernelArgs {
   float* ws_acc;   // [W + batch][Hq][HD] unnormalised partial outputs (workspace)
   float* ws_ml;    // [W + batch][Hq][2] partial (m, l) (workspace)
   uint16_t* out;
+  // Fused store (STORE kernels only): the step's new K/V rows [batch][Hkv][HD] with token strides in
+  // elements, and an optional slot_mapping output.
+  const uint16_t* knew;
+  int64_t knew_stride;
+  const uint16_t* vnew;
+  int64_t vnew_stride;
+  int32_t* slot_out;
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeKernelArgs& p, int b) {
@@ -102,14 +115,30 @@ __global__ void __launch_bounds__(1024) decode_prefix_kernel(DecodeKernelArgs p)
   if (threadIdx.x == 0) p.cu[p.batch] = carry;
 }
 
+// A wave-uniform 64-bit value held in SGPRs (values read from LDS arrive in VGPRs).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ int64_t range_begin(int64_t T, int W, int w) { return T * w / W; }
 
 // The worker whose range holds global key index x (ranges are [range_begin(w), range_begin(w + 1))).
 __device__ __forceinline__ int worker_of(int64_t T, int W, int64_t x) { return int(((x + 1) * W - 1) / T); }
 
-template <int G>
-__global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKernelArgs p) {
+template <int G, bool STORE>
+__global__ void __launch_bounds__(64 * MAX_WAVES) __attribute__((amdgpu_waves_per_eu(G <= 2 ? 3 : 2)))
+decode_lean_kernel(DecodeKernelArgs p) {
   const int w = blockIdx.y, W = p.workers;
+  if (STORE && p.slot_out && blockIdx.x == 0 && blockIdx.y == 0) {
+    // The step's slot_mapping: position context_lens[b] - 1 through the block table, -1 when there is none.
+    for (int i = threadIdx.x; i < p.batch; i += blockDim.x) {
+      const int pos = p.ctx[i] - 1, lb = pos >= 0 ? pos / p.bs : 0;
+      const int blk = pos >= 0 && lb < p.max_blocks ? p.bt[int64_t(i) * p.max_blocks + lb] : -1;
+      p.slot_out[i] = blk >= 0 ? blk * p.bs + pos % p.bs : -1;
+    }
+  }
   // Prefix sums of the clamped context lengths.  Up to LDS_CU_MAX - 1 sequences every work-group scans them
   // into LDS itself (a few hundred cycles, and one kernel launch less); the first work-group also stores them
   // for the combine kernel.  Larger batches read the sums decode_prefix_kernel wrote.
@@ -165,13 +194,13 @@ __global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKerne
       const int mid = (lo + hi) >> 1;
       if ((cu_in_lds ? s_cu[mid] : p.cu[mid]) <= x) lo = mid; else hi = mid;
     }
-    b = lo;
+    b = __builtin_amdgcn_readfirstlane(lo);  // uniform: keep it (and what derives from it) in SGPRs
   }
   if (kvh >= p.num_kv_heads) return;
 
   while (x < x_end && b < p.batch) {
-    const int64_t seq0 = cu_in_lds ? s_cu[b] : p.cu[b];
-    const int64_t seq1 = cu_in_lds ? s_cu[b + 1] : p.cu[b + 1];
+    const int64_t seq0 = uniform64(cu_in_lds ? s_cu[b] : p.cu[b]);
+    const int64_t seq1 = uniform64(cu_in_lds ? s_cu[b + 1] : p.cu[b + 1]);
     if (seq1 <= x) {  // empty sequence
       ++b;
       continue;
@@ -180,7 +209,26 @@ __global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKerne
     const int t0 = int(x - seq0);
     const int t1 = int(min(x_end, seq1) - seq0);
     const int32_t* bt_row = p.bt + int64_t(b) * p.max_blocks;
-
+    // Fused store: when this range ends the sequence and the context was not clamped, key ctx - 1 is the step's
+    // new token; its rows go to the cache before any key of the sequence is read (lanes 0-15 of the wave move
+    // its kv head's K row, lanes 16-31 the V row, 16 bytes each).
+    if (STORE && t1 == ctx && p.ctx[b] == ctx) {
+      const int tn = ctx - 1;
+      const int blk = bt_row[tn / bs];
+      if (blk >= 0 && blk < p.num_blocks && lane < 32) {
+        const int64_t dst = (int64_t(blk) * bs + tn % bs) * slot_elems + kvh * HD + (lane & 15) * 8;
+        const bool is_k = lane < 16;
+        const uint16_t* src = (is_k ? p.knew + int64_t(b) * p.knew_stride : p.vnew + int64_t(b) * p.vnew_stride) +
+                              kvh * HD + (lane & 15) * 8;
+        const u32x4 row = *reinterpret_cast<const u32x4*>(src);
+        uint16_t* cache = const_cast<uint16_t*>(is_k ? p.kc : p.vc);
+        *reinterpret_cast<u32x4*>(cache + dst) = row;
+      }
+      // The write completes (s_waitcnt vmcnt(0): acknowledged by L2) before this wave's loads below, whose lanes
+      // of another group read the slot; the fence keeps the compiler from moving those loads above it.
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     // This lane's 16 query dims (sub*8 .. +8 and 64 + sub*8 .. +8) of each head in the group, as bf16 pairs.
     uint32_t qa[G][4], qb[G][4];
 #pragma unroll
@@ -204,7 +252,7 @@ __global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKerne
     // Slot of this lane's token u in the iteration starting at `base` (token base + 8 u + grp).  A token
     // past the range reads the range's first token instead (a real, finite row whose weight is 0, where
     // 0 * stale or poisoned data could be NaN); an unusable block-table entry reads slot 0 and is masked.
-    int64_t slot_n[4];
+    int64_t off_n[4];  // element offset of the token's K (and V) row from the cache bases
     bool ok_n[4];
     auto locate = [&](int base) {
 #pragma unroll
@@ -222,7 +270,7 @@ __global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKerne
         const int blk = bt_row[lb];
         const bool usable = blk >= 0 && blk < p.num_blocks;
         ok_n[u] = usable && t < t1;
-        slot_n[u] = usable ? int64_t(blk) * bs + cell : 0;
+        off_n[u] = usable ? (int64_t(blk) * bs + cell) * slot_elems : 0;
       }
     };
     locate(t0);
@@ -232,7 +280,7 @@ __global__ void __launch_bounds__(64 * MAX_WAVES) decode_lean_kernel(DecodeKerne
       bool ok[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int64_t off = slot_n[u] * slot_elems;
+        const int64_t off = off_n[u];
         ok[u] = ok_n[u];
         ka[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
         kb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off + 64));
@@ -408,7 +456,7 @@ Layout workspace_layout(int batch, int num_q_heads) {
 
 // W: as many work-groups as the device keeps resident at once (cached per device and kernel shape).
 int resident_workers(const void* kernel, int threads, int key) {
-  static int cached[64][3][MAX_WAVES + 1] = {};
+  static int cached[64][6][MAX_WAVES + 1] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   int& slot = cached[dev][key][threads / 64];
@@ -434,7 +482,7 @@ int device_cus() {
   return cus;
 }
 
-template <int G, int KEY>
+template <int G, int KEY, bool STORE>
 hipError_t launch_g(DecodeKernelArgs& p, hipStream_t stream) {
   const int waves = std::min(MAX_WAVES, p.num_kv_heads);
   const int threads = 64 * waves;
@@ -443,12 +491,13 @@ hipError_t launch_g(DecodeKernelArgs& p, hipStream_t stream) {
   // two halves of the same token rows at the same time.  W = 2 per CU, within one resident round: enough
   // loads in flight to saturate HBM (measured on MI355X, batch 64: 1024 / 768 / 512 / 256 workers reach
   // 4.93 / 5.07 / 5.14 / 4.99 TB/s; fewer workers also mean fewer partial outputs to merge).
-  const int resident = resident_workers(reinterpret_cast<const void*>(&decode_lean_kernel<G>), threads, KEY);
+  const int resident =
+      resident_workers(reinterpret_cast<const void*>(&decode_lean_kernel<G, STORE>), threads, KEY + (STORE ? 3 : 0));
   p.workers = std::max(1, std::min(resident / head_groups, 2 * device_cus()));
   const bool cu_in_lds = p.batch + 1 <= LDS_CU_MAX;
   if (!cu_in_lds) hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, p);
   const size_t lds = cu_in_lds ? size_t(p.batch + 1 + threads) * sizeof(int64_t) : 0;
-  hipLaunchKernelGGL(decode_lean_kernel<G>, dim3(head_groups, p.workers), dim3(threads), lds, stream, p);
+  hipLaunchKernelGGL((decode_lean_kernel<G, STORE>), dim3(head_groups, p.workers), dim3(threads), lds, stream, p);
   hipLaunchKernelGGL(decode_combine_kernel, dim3(p.num_q_heads, p.batch), dim3(HD), 0, stream, p);
   return hipGetLastError();
 }
@@ -465,7 +514,8 @@ DecodePlan decode_plan(int batch, int num_q_heads, int /*num_kv_heads*/, int /*m
   return plan;
 }
 
-hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t stream) {
+hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t stream,
+                              const DecodeStoreArgs* fused) {
   (void)plan;
   const Layout L = workspace_layout(a.batch, a.num_q_heads);
   char* ws = static_cast<char*>(workspace);
@@ -489,8 +539,17 @@ hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* w
   p.ws_acc = reinterpret_cast<float*>(ws + L.acc);
   p.ws_ml = reinterpret_cast<float*>(ws + L.ml);
   p.out = static_cast<uint16_t*>(a.out);
+  p.knew = fused ? static_cast<const uint16_t*>(fused->k_new) : nullptr;
+  p.knew_stride = fused ? fused->k_new_stride : 0;
+  p.vnew = fused ? static_cast<const uint16_t*>(fused->v_new) : nullptr;
+  p.vnew_stride = fused ? fused->v_new_stride : 0;
+  p.slot_out = fused ? fused->slot_out : nullptr;
   const int group = a.num_q_heads / a.num_kv_heads;
-  return group == 1 ? launch_g<1, 0>(p, stream) : group == 2 ? launch_g<2, 1>(p, stream) : launch_g<4, 2>(p, stream);
+  if (fused)
+    return group == 1 ? launch_g<1, 0, true>(p, stream)
+                      : group == 2 ? launch_g<2, 1, true>(p, stream) : launch_g<4, 2, true>(p, stream);
+  return group == 1 ? launch_g<1, 0, false>(p, stream)
+                    : group == 2 ? launch_g<2, 1, false>(p, stream) : launch_g<4, 2, false>(p, stream);
 }
 
 }  // namespace pkv

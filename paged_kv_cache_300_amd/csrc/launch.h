@@ -51,7 +51,20 @@ struct DecodePlan {
 };
 bool decode_fast_supported(int head_dim, int group, bool bf16);
 DecodePlan decode_plan(int batch, int num_q_heads, int num_kv_heads, int max_ctx);
-hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t stream);
+// The step's new K/V rows for the fused store + decode (token strides in elements; slot_out may be NULL).
+struct DecodeStoreArgs {
+  const void* k_new; int64_t k_new_stride;
+  const void* v_new; int64_t v_new_stride;
+  int32_t* slot_out;
+};
+// fused == NULL: decode over the cache as it is; else the new token of each row is stored and attended too.
+hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t stream,
+                              const DecodeStoreArgs* fused = nullptr);
+// Any dtype and shape: the new token of each decode row to its slot (context_lens[b] - 1 through the block
+// table), optionally writing slot_mapping; rows with no slot write nothing.
+hipError_t launch_decode_store(const DecodeStoreArgs& s, const int32_t* context_lens, const int32_t* block_tables,
+                               int batch, int max_blocks, int block_size, int num_blocks, void* k_cache,
+                               void* v_cache, int row_elems, int elem_bytes, hipStream_t stream);
 
 // bf16, head_dim 128 prefill on MFMA.
 bool prefill_fast_supported(int head_dim, int group, bool bf16);

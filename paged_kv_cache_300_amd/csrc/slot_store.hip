@@ -49,6 +49,38 @@ __global__ void slot_mapping_decode_kernel(const int32_t* __restrict__ ctx, cons
   out[t] = t < batch ? slot_of_position(bt + int64_t(t) * max_blocks, max_blocks, block_size, ctx[t] - 1) : -1;
 }
 
+// Decode store of any shape: row b's new token (position context_lens[b] - 1) to its slot, one work-group per
+// row copying the K and V rows in 2-byte units; the slot is also written to slot_out when given.  A position
+// with no usable block (outside the table, a negative entry, a block past the cache) writes nothing.
+__global__ void __launch_bounds__(256) decode_store_kernel(DecodeStoreArgs s, const int32_t* __restrict__ ctx,
+                                                           const int32_t* __restrict__ bt, int max_blocks,
+                                                           int block_size, int64_t num_slots, uint16_t* k_cache,
+                                                           uint16_t* v_cache, int row_units, int elem_units) {
+  const int b = blockIdx.x;
+  const int32_t slot = slot_of_position(bt + int64_t(b) * max_blocks, max_blocks, block_size, ctx[b] - 1);
+  if (threadIdx.x == 0 && s.slot_out) s.slot_out[b] = slot;
+  if (slot < 0 || slot >= num_slots) return;
+  const uint16_t* kr = static_cast<const uint16_t*>(s.k_new) + int64_t(b) * s.k_new_stride * elem_units;
+  const uint16_t* vr = static_cast<const uint16_t*>(s.v_new) + int64_t(b) * s.v_new_stride * elem_units;
+  uint16_t* kd = k_cache + int64_t(slot) * row_units;
+  uint16_t* vd = v_cache + int64_t(slot) * row_units;
+  for (int i = threadIdx.x; i < row_units; i += blockDim.x) {
+    kd[i] = kr[i];
+    vd[i] = vr[i];
+  }
+}
+
+hipError_t launch_decode_store(const DecodeStoreArgs& s, const int32_t* context_lens, const int32_t* block_tables,
+                               int batch, int max_blocks, int block_size, int num_blocks, void* k_cache,
+                               void* v_cache, int row_elems, int elem_bytes, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const int elem_units = elem_bytes / 2;
+  hipLaunchKernelGGL(decode_store_kernel, dim3(batch), dim3(256), 0, stream, s, context_lens, block_tables,
+                     max_blocks, block_size, int64_t(num_blocks) * block_size, static_cast<uint16_t*>(k_cache),
+                     static_cast<uint16_t*>(v_cache), row_elems * elem_units, elem_units);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(const int32_t* cu_q, const int32_t* cu_k, const int32_t* ctx_lens,
                                const int32_t* block_tables, int batch, int max_blocks, int block_size,
                                int num_tokens, int32_t* slot_mapping, hipStream_t stream) {

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for fn in ("kv_slot_mapping", "kv_store", "kv_store_qk_norm_rope", "attn_prefill_varlen",
                "attn_prefill_workspace_bytes",
-               "attn_decode_paged", "attn_decode_workspace_bytes", "pkv_last_error"):
+               "attn_decode_paged", "attn_decode_paged_store", "attn_decode_workspace_bytes", "pkv_last_error"):
         assert fn in names
 
 
@@ -71,6 +71,21 @@ def test_qk_norm_rope_store_rejects_bad_arguments_on_host():
     assert L.kv_store_qk_norm_rope(*args(128, 1e-6, 0.0, 16 * 128)) == -1        # theta must be > 0
     assert L.kv_store_qk_norm_rope(*args(128, 1e-6, 1e6, 15 * 128)) == -1        # q stride shorter than a row
     assert "stride" in _err(L)
+
+
+def test_fused_decode_store_rejects_bad_arguments_on_host():
+    pkv, L = _lib()
+    fake = ctypes.c_void_p(0x1000)
+    need = L.attn_decode_workspace_bytes(64, 16, 8, 128, 16, 256, pkv.PKV_BF16)
+
+    def call(ks=1024, vs=1024, knew=fake, ws=need, num_blocks=4096):
+        return L.attn_decode_paged_store(fake, 2048, knew, ks, fake, vs, fake, fake, num_blocks, fake, fake, 64, 16,
+                                         256, 16, 8, 128, 0.088, fake, None, fake, ws, pkv.PKV_BF16, None)
+    assert call(ks=1000) == -1 and "k_new_stride" in _err(L)       # new-row stride shorter than a row
+    assert call(vs=0) == -1
+    assert call(knew=None) == -1 and "k_new" in _err(L)            # no new rows
+    assert call(ws=need - 1) == -3 and "workspace" in _err(L)      # same workspace rule as attn_decode_paged
+    assert call(num_blocks=2 ** 23 + 1) == -2                      # slots past int32
 
 
 def test_slot_mapping_rejects_bad_arguments_on_host():

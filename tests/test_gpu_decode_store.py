@@ -1,0 +1,148 @@
+"""GPU parity of the fused decode step (attn_decode_paged_store): the cache bytes and slot_mapping equal those of
+kv_slot_mapping + kv_store bit for bit, and the output meets the float64 oracle's tolerance (bf16 2e-2, float32
+1e-5) and agrees with the unfused attn_decode_paged to the same bar."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (BF16_TOL, F32_TOL, gpu_store_history, i32, log, max_abs_err, nan_cache, oracle_attention,
+                      oracle_slot_mapping, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_300_amd as m
+    m.lib()
+    return m
+
+
+def _tol(dtype):
+    return BF16_TOL if dtype == "bf16" else F32_TOL
+
+
+def _bits(t):
+    t = t.detach().contiguous()
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _both(pkv, case, block_tables=None, k_new=None, v_new=None, with_slots=True, zero_fill=False):
+    """Unfused step (slot_mapping, store, decode) and fused step on two copies of one cache (free cells
+    NaN-poisoned, or zero with ``zero_fill``)."""
+    kc, vc = nan_cache(case), nan_cache(case)
+    if zero_fill:
+        kc.zero_()
+        vc.zero_()
+    gpu_store_history(case, kc, vc)
+    kc2, vc2 = kc.clone(), vc.clone()
+    bt = i32(case.block_tables if block_tables is None else block_tables)
+    ctx = i32(case.context_lens)
+    q = to_dev(case.q, case.dtype)
+    k = to_dev(case.k, case.dtype) if k_new is None else k_new
+    v = to_dev(case.v, case.dtype) if v_new is None else v_new
+    sm = pkv.kv_slot_mapping(bt, case.block_size, case.batch, context_lens=ctx)
+    pkv.kv_store(k, v, kc, vc, sm)
+    out = pkv.attn_decode_paged(q, kc, vc, ctx, bt, case.scale)
+    sm2 = torch.full((case.batch,), -7, dtype=torch.int32, device="cuda") if with_slots else None
+    out2 = pkv.attn_decode_paged_store(q, k, v, kc2, vc2, ctx, bt, case.scale, slot_mapping_out=sm2)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(kc), _bits(kc2)), "k cache differs from kv_store's"
+    assert torch.equal(_bits(vc), _bits(vc2)), "v cache differs from kv_store's"
+    if with_slots:
+        assert torch.equal(sm, sm2), "slot_mapping differs from kv_slot_mapping's"
+    diff = float((out.float() - out2.float()).abs().max()) if out.numel() else 0.0
+    log(f"  fused vs unfused output max-abs {diff:.3e}")
+    assert diff <= _tol(case.dtype)
+    return out2, sm
+
+
+def _check_oracle(case, out, rows=None):
+    want = oracle_attention(case, rows)
+    got = oracle.as_f64(to_host(out), case.dtype)
+    worst = max((max_abs_err(got[b:b + 1], w) for b, w in want.items()), default=0.0)
+    log(f"  oracle max-abs {worst:.3e} (tol {_tol(case.dtype):.0e})")
+    assert worst <= _tol(case.dtype)
+
+
+CASES = [
+    # (dtype, hq, hkv, hd, bs, context lengths, seed)
+    ("bf16", 16, 8, 128, 256, [1, 2, 255, 256, 257, 600, 1000, 1300], 201),
+    ("bf16", 16, 8, 128, 16, [5, 100, 1029, 31, 0, 300], 202),
+    ("bf16", 8, 8, 128, 3, [7, 64, 300, 1], 203),      # one query head per kv head
+    ("bf16", 16, 4, 128, 1, [65, 200, 3], 204),        # groups of 4
+    ("bf16", 16, 2, 128, 32, [700, 33], 205),          # group of 8: store kernel + generic decode
+    ("bf16", 8, 4, 64, 8, [100, 9, 513], 206),         # head_dim 64: store kernel + generic decode
+    ("bf16", 16, 8, 128, 256, [0, 0, 0], 207),         # all padding
+    ("bf16", 16, 8, 128, 4, [1, 2, 0], 208),           # fewer keys than workers
+    ("f32", 4, 2, 16, 4, [1, 7, 30, 100], 209),        # the tiny fp32 layer's shape
+    ("f32", 16, 8, 128, 256, [300, 1], 210),
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,hd,bs,ctx,seed", CASES)
+def test_fused_decode_step(pkv, dtype, hq, hkv, hd, bs, ctx, seed):
+    case = workloads.decode_case(ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, block_size=bs,
+                                 num_blocks=sum(math.ceil(c / bs) for c in ctx) + 3, dtype=dtype, seed=seed,
+                                 max_blocks=max(math.ceil(c / bs) for c in ctx) + 1)
+    log(f"fused decode {dtype} {hq}/{hkv}/{hd} bs={bs} ctx={ctx}")
+    out, sm = _both(pkv, case)
+    np.testing.assert_array_equal(to_host(sm), oracle_slot_mapping(case))
+    _check_oracle(case, out)
+    for b in np.where(np.asarray(ctx) == 0)[0]:
+        assert bool((out[int(b)] == 0).all())
+
+
+@pytest.mark.parametrize("batch,ctx_len", [(384, 1), (768, 1), (384, 2), (1000, 3)])
+def test_ranges_that_start_at_the_new_token(pkv, batch, ctx_len):
+    """Equal short contexts: the workers' key ranges start at (or next to) a new token, whose stand-in reads
+    past a range end must come from the step's rows, not from the still unwritten (NaN) slot."""
+    case = workloads.decode_case([ctx_len] * batch, num_blocks=batch + 2, block_size=16, seed=211 + ctx_len,
+                                 max_blocks=1)
+    log(f"fused decode batch {batch} x ctx {ctx_len}")
+    out, _ = _both(pkv, case)
+    assert bool(torch.isfinite(out.float()).all())
+    _check_oracle(case, out, rows=list(range(0, batch, 37)) + [batch - 1])
+
+
+def test_workload2_decode_shape(pkv):
+    """Workload 2 (batch 64, context lengths U[512, 4096], 4096-block cache): sampled rows against the oracle."""
+    case = workloads.workload2()
+    log(f"fused decode, workload 2: sum ctx {int(case.Lk.sum())}")
+    out, _ = _both(pkv, case)
+    _check_oracle(case, out, rows=[0, 17, 40, 63])
+
+
+def test_unusable_entries_and_clamped_contexts(pkv):
+    """A new token whose block-table entry is -1 or past the cache, and a context longer than the table: no
+    store (slot -1, or a slot past the cache), the same caches and outputs as the unfused step."""
+    ctx = [40, 70, 100, 112, 9]
+    case = workloads.decode_case(ctx, num_blocks=40, block_size=16, seed=221, max_blocks=7)
+    bt = case.block_tables.copy()
+    bt[0, (40 - 1) // 16] = -1          # the new token's block: none
+    bt[1, (70 - 1) // 16] = 40 + 5      # the new token's block: past the cache
+    case.Lk = np.array([40, 70, 100, 200, 9], dtype=np.int32)  # row 3 longer than its 7-block table: clamped to 112
+    log("fused decode with unusable block-table entries and a clamped context")
+    out, sm = _both(pkv, case, block_tables=bt, zero_fill=True)  # row 3 reads a slot nobody wrote
+    got = to_host(sm)
+    assert got[0] == -1 and got[3] == -1 and got[1] == (40 + 5) * 16 + (69 % 16)
+    assert bool(torch.isfinite(out.float()).all())
+    _check_oracle(case, out, rows=[2, 4])
+
+
+def test_new_rows_from_a_merged_projection(pkv):
+    """k_new / v_new as strided views of one [B, (Hq + 2 Hkv) hd] buffer; no slot_mapping output."""
+    ctx = [300, 1, 77, 1024]
+    case = workloads.decode_case(ctx, num_blocks=12, seed=231, max_blocks=5)
+    b = case.batch
+    merged = np.concatenate([case.q.reshape(b, -1), case.k.reshape(b, -1), case.v.reshape(b, -1)], axis=1)
+    dev = to_dev(merged, "bf16")
+    k = dev[:, 2048:3072].view(b, 8, 128)
+    v = dev[:, 3072:].view(b, 8, 128)
+    out, _ = _both(pkv, case, k_new=k, v_new=v, with_slots=False)
+    _check_oracle(case, out)
