@@ -210,25 +210,24 @@ decode_lean_kernel(DecodeKernelArgs p) {
     const int t1 = int(min(x_end, seq1) - seq0);
     const int32_t* bt_row = p.bt + int64_t(b) * p.max_blocks;
     // Fused store: when this range ends the sequence and the context was not clamped, key ctx - 1 is the step's
-    // new token; its rows go to the cache before any key of the sequence is read (lanes 0-15 of the wave move
-    // its kv head's K row, lanes 16-31 the V row, 16 bytes each).
+    // new token, whose rows must reach the cache before this wave reads that slot (lanes 0-15 of the wave move
+    // its kv head's K row, lanes 16-31 the V row, 16 bytes each).  The rows are loaded here, next to the
+    // query and block-table loads the first iteration waits for anyway, written at the top of the first
+    // iteration, and the write is waited for at the top of the iteration that reads the slot (the last one).
+    int new_blk = -1;  // cache block of the pending write, -1: none
+    u32x4 new_row = {0, 0, 0, 0};
     if (STORE && t1 == ctx && p.ctx[b] == ctx) {
-      const int tn = ctx - 1;
-      const int blk = bt_row[tn / bs];
-      if (blk >= 0 && blk < p.num_blocks && lane < 32) {
-        const int64_t dst = (int64_t(blk) * bs + tn % bs) * slot_elems + kvh * HD + (lane & 15) * 8;
-        const bool is_k = lane < 16;
-        const uint16_t* src = (is_k ? p.knew + int64_t(b) * p.knew_stride : p.vnew + int64_t(b) * p.vnew_stride) +
-                              kvh * HD + (lane & 15) * 8;
-        const u32x4 row = *reinterpret_cast<const u32x4*>(src);
-        uint16_t* cache = const_cast<uint16_t*>(is_k ? p.kc : p.vc);
-        *reinterpret_cast<u32x4*>(cache + dst) = row;
+      const int blk = bt_row[(ctx - 1) / bs];
+      if (blk >= 0 && blk < p.num_blocks) {
+        new_blk = blk;
+        if (lane < 32) {
+          const uint16_t* src = (lane < 16 ? p.knew + int64_t(b) * p.knew_stride : p.vnew + int64_t(b) * p.vnew_stride) +
+                                kvh * HD + (lane & 15) * 8;
+          new_row = *reinterpret_cast<const u32x4*>(src);
+        }
       }
-      // The write completes (s_waitcnt vmcnt(0): acknowledged by L2) before this wave's loads below, whose lanes
-      // of another group read the slot; the fence keeps the compiler from moving those loads above it.
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-      __builtin_amdgcn_s_waitcnt(0);
     }
+    bool wrote = false;  // the new rows were written and not yet waited for
     // This lane's 16 query dims (sub*8 .. +8 and 64 + sub*8 .. +8) of each head in the group, as bf16 pairs.
     uint32_t qa[G][4], qb[G][4];
 #pragma unroll
@@ -276,6 +275,22 @@ decode_lean_kernel(DecodeKernelArgs p) {
     locate(t0);
 
     for (int base = t0; base < t1; base += WAVE_TOKENS) {
+      if (STORE && new_blk >= 0) {  // first iteration: the rows arrived with the block-table entries
+        if (lane < 32) {
+          const int64_t dst = (int64_t(new_blk) * bs + (ctx - 1) % bs) * slot_elems + kvh * HD + (lane & 15) * 8;
+          uint16_t* cache = const_cast<uint16_t*>(lane < 16 ? p.kc : p.vc);
+          *reinterpret_cast<u32x4*>(cache + dst) = new_row;
+        }
+        new_blk = -1;
+        wrote = true;
+      }
+      if (STORE && wrote && base + WAVE_TOKENS >= t1) {
+        // The write completes (s_waitcnt vmcnt(0): acknowledged by L2) before the loads below, whose lanes of
+        // another group read the slot; the fence keeps the compiler from moving those loads above it.
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        __builtin_amdgcn_s_waitcnt(0);
+        wrote = false;
+      }
       u32x4 ka[4], kb[4], va[4], vb[4];
       bool ok[4];
 #pragma unroll
