@@ -2,20 +2,23 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
 Headline: one decode layer-step of workload 2 (batch 64, context_lens U[512,4096], block_size 256, bf16,
-16 q / 8 kv heads, head_dim 128): kv_slot_mapping -> kv_store of the new token -> attn_decode_paged.
-``value`` is the KV-cache bytes the decode must read (sum(context_lens) * 2 * Hkv * hd * 2 B) divided by the
-whole step's time.  Steps rotate over ``--layers`` independent caches (different layers of the model), so
-the 256 MB Infinity Cache cannot hold the working set between steps.
+16 q / 8 kv heads, head_dim 128): slot_mapping, the store of each sequence's new token and the paged decode
+attention, in one attn_decode_paged_store call (the same results as kv_slot_mapping -> kv_store ->
+attn_decode_paged, which is measured too, under ``secondary``).  ``value`` is the KV-cache bytes the decode
+must read (sum(context_lens) * 2 * Hkv * hd * 2 B) divided by the whole step's time.  Steps rotate over
+``--layers`` independent caches (different layers of the model), so the 256 MB Infinity Cache cannot hold
+the working set between steps.
 
 The same JSON line carries:
-  roofline      the decode attention call (split + combine kernels) timed with two HIP events on the stream
-                it runs on around K back-to-back calls over the same rotated caches (an event record per
-                call would make the GPU drain before each one), against MI355X's 8 TB/s HBM peak;
-                ``traffic`` from rocprofv3 counters kept in profiles/ (null if the kernel source changed
-                since they were taken);
+  roofline      the step's call (split + combine kernels) timed with two HIP events on the stream it runs
+                on around K back-to-back calls over the same rotated caches (an event record per call would
+                make the GPU drain before each one), against MI355X's 8 TB/s HBM peak; ``traffic`` from
+                rocprofv3 counters kept in profiles/ (null if the kernel source changed since they were
+                taken);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, BLAS pinned to one thread;
-  secondary     varlen prefill TFLOP/s (workload 3), prefix-cache prefill TFLOP/s (workload 4), the store
-                sweep GB/s (workload 5, N=16384) and the long padded decode GB/s (workload 5, batch 256).
+  secondary     the unfused decode step and call, varlen prefill TFLOP/s (workload 3), prefix-cache prefill
+                TFLOP/s (workload 4), the store sweep GB/s (workload 5, N=16384), the long padded decode GB/s
+                (workload 5, batch 256) and the fused QK-Norm + RoPE + store GB/s (workload 3's tokens).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
 """
@@ -311,7 +314,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope", "fused_decode"],
+    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope", "unfused_decode"],
                     default=None,
                     help="run just one secondary workload (after the headline), e.g. for a profiler")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -327,24 +330,25 @@ def main():
     pkv.lib()
     torch.cuda.set_device(0)
 
-    log("decode, workload 2")
-    dec = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers)
+    log("decode step (fused store + decode), workload 2")
+    dec = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers, fused=True)
     achieved = dec["kv_bytes"] / (dec["kernel_ms"] * 1e-3) / 1e9
     value = dec["kv_bytes"] / (dec["wall_ms"] * 1e-3) / 1e9
     dec_hash = source_hash("attn_decode.hip", "common.h")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("attn_decode_workload2", dec_hash),
-                "kernel": "attn_decode_paged (decode_lean_kernel + decode_combine_kernel)", "kernel_ms": round(dec["kernel_ms"], 5),
-                "algorithmic_bytes": dec["kv_bytes"], "source_hash": dec_hash}
+                "traffic": measured_traffic("attn_decode_paged_store_workload2", dec_hash),
+                "kernel": "attn_decode_paged_store (decode_lean_kernel<2, store> + decode_combine_kernel)",
+                "kernel_ms": round(dec["kernel_ms"], 5), "algorithmic_bytes": dec["kv_bytes"],
+                "source_hash": dec_hash}
 
     secondary = {}
     if not args.headline_only:
         want = lambda name: args.only in (None, name)
         p3 = p4 = st = d5 = qr = fd = None
-        if want("fused_decode"):
-            log("fused store + decode step, workload 2")
-            fd = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers, fused=True)
+        if want("unfused_decode"):
+            log("unfused decode step (slot_mapping, store, decode), workload 2")
+            fd = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers)
         if want("prefill"):
             log("prefill, workload 3")
             p3 = bench_prefill(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers, paged=False)
@@ -374,11 +378,12 @@ def main():
                                                  "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
                                                  "tokens": st["tokens"]}
         if fd is not None:
-            secondary["decode_step_fused_workload2"] = {
+            gbk = fd["kv_bytes"] / (fd["kernel_ms"] * 1e-3) / 1e9
+            secondary["decode_step_unfused_workload2"] = {
                 "value": round(fd["kv_bytes"] / (fd["wall_ms"] * 1e-3) / 1e9, 1), "unit": "GB/s",
-                "step_ms": round(fd["wall_ms"], 5), "kernel_ms": round(fd["kernel_ms"], 5),
-                "kernel_GBps": round(fd["kv_bytes"] / (fd["kernel_ms"] * 1e-3) / 1e9, 1),
-                "step": "attn_decode_paged_store (slot_mapping + store + decode in one call)"}
+                "step_ms": round(fd["wall_ms"], 5), "call_ms": round(fd["kernel_ms"], 5),
+                "call_GBps": round(gbk, 1), "call_frac_hbm_peak": round(gbk / HBM_PEAK_GBS, 4),
+                "step": "kv_slot_mapping + kv_store + attn_decode_paged (call = attn_decode_paged alone)"}
         if qr is not None:
             gbq = qr["bytes"] / (qr["kernel_ms"] * 1e-3) / 1e9
             secondary["qknorm_rope_store_workload3"] = {"value": round(gbq, 1), "unit": "GB/s",
@@ -412,7 +417,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workloads.WORKLOADS[2], "batch": dec["batch"], "sum_context_lens": dec["sum_ctx"],
                    "heads": "16 q / 8 kv", "head_dim": 128, "block_size": 256, "layers_rotated": args.layers,
-                   "step": "kv_slot_mapping + kv_store + attn_decode_paged"},
+                   "step": "attn_decode_paged_store (slot_mapping + store of the new token + paged decode)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,
