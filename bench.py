@@ -233,6 +233,57 @@ def bench_store(pkv, torch, steps, warmup):
     return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n}
 
 
+def bench_decode_latency(pkv, torch, reps):
+    """The decode step (attn_decode_paged_store) at fixed batch sizes, the batch padded up to each with rows of
+    context 0 (slot -1), launched eagerly and replayed from a HIP graph captured once per size: time per step
+    back to back, and one step's latency from launch to completion as the host sees it."""
+    import numpy as np
+    import workloads
+    res = {}
+    for real, bucket in ((1, 1), (5, 8), (24, 32), (64, 64), (200, 256)):
+        rng = np.random.default_rng(40 + bucket)
+        ctx = np.concatenate([rng.integers(512, 4096, size=real, endpoint=True), np.zeros(bucket - real, np.int64)])
+        case = workloads.decode_case(ctx, num_blocks=int(sum(math.ceil(int(c) / 256) for c in ctx)) + 2,
+                                     seed=41 + bucket, device="cuda", max_blocks=16, rng=rng)
+        kc, vc = build_caches(pkv, torch, case)
+        bt = torch.from_numpy(case.block_tables).cuda()
+        cl = torch.from_numpy(case.context_lens).cuda()
+        ws = torch.empty(max(pkv.attn_decode_workspace_bytes(bucket, 16, 8, 128, 16, 256), 1), dtype=torch.uint8,
+                         device="cuda")
+        o = torch.empty_like(case.q)
+        sm = torch.empty(bucket, dtype=torch.int32, device="cuda")
+
+        def step():
+            pkv.attn_decode_paged_store(case.q, case.k, case.v, kc, vc, cl, bt, case.scale, out=o, workspace=ws,
+                                        slot_mapping_out=sm)
+
+        def single(fn):
+            times = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                times.append(time.perf_counter() - t0)
+            return sorted(times)[len(times) // 2] * 1e6
+
+        step()
+        torch.cuda.synchronize()
+        eager = run_steps(torch, lambda i: step(), reps, 5) * 1e3
+        eager_one = single(step)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        graph = run_steps(torch, lambda i: g.replay(), reps, 5) * 1e3
+        graph_one = single(g.replay)
+        res[str(bucket)] = {"real_rows": real, "kv_MB": round(int(ctx.sum()) * 4096 / 1e6, 1),
+                            "eager_us_per_step": round(eager, 1), "graph_us_per_step": round(graph, 1),
+                            "eager_us_one_step": round(eager_one, 1), "graph_us_one_step": round(graph_one, 1)}
+        del g, kc, vc, case
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_qknorm_rope_store(pkv, torch, make, steps, warmup, layers):
     """The fused QK-Norm + RoPE + store over one prefill step's new tokens (workload 3's q, k, v)."""
     cases, _ = dev_case_layers(make, layers, torch)
@@ -314,7 +365,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope", "unfused_decode"],
+    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope", "unfused_decode",
+                                       "decode_latency"],
                     default=None,
                     help="run just one secondary workload (after the headline), e.g. for a profiler")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -345,7 +397,7 @@ def main():
     secondary = {}
     if not args.headline_only:
         want = lambda name: args.only in (None, name)
-        p3 = p4 = st = d5 = qr = fd = None
+        p3 = p4 = st = d5 = qr = fd = dl = None
         if want("unfused_decode"):
             log("unfused decode step (slot_mapping, store, decode), workload 2")
             fd = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers)
@@ -361,6 +413,9 @@ def main():
         if want("qknorm_rope"):
             log("QK-Norm + RoPE + store, workload 3's tokens")
             qr = bench_qknorm_rope_store(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers)
+        if want("decode_latency"):
+            log("decode step latency at padded fixed batch sizes, eager and graph")
+            dl = bench_decode_latency(pkv, torch, max(args.steps, 20))
         if want("long_decode"):
             log("long padded decode, workload 5")
             d5 = bench_decode(pkv, torch, workloads.workload5_decode, max(args.steps // 5, 3), 2, 2)
@@ -390,6 +445,8 @@ def main():
                                                        "frac_hbm_peak": round(gbq / HBM_PEAK_GBS, 4),
                                                        "kernel_ms": round(qr["kernel_ms"], 5), "bytes": qr["bytes"],
                                                        "tokens": qr["tokens"]}
+        if dl is not None:
+            secondary["decode_step_latency_padded_batches"] = dl
         if d5 is not None:
             gbs5 = d5["kv_bytes"] / (d5["kernel_ms"] * 1e-3) / 1e9
             secondary["long_decode_workload5"] = {"value": round(gbs5, 1), "unit": "GB/s",

@@ -101,3 +101,67 @@ def test_prefix_prefill_graph_replays(pkv):
     err = max(max_abs_err(got[int(case.cu_seqlens_q[b]):int(case.cu_seqlens_q[b + 1])], w) for b, w in want.items())
     log(f"prefill eager max-abs {err:.3e}")
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("real,bucket", [(5, 8), (64, 64), (200, 256)])
+def test_padded_fixed_batch_decode_loop_in_a_graph(pkv, real, bucket):
+    """The serving pattern the -1 slot exists for: one decode step (attn_decode_paged_store) captured at a fixed
+    batch size, the batch padded up to it with rows of context 0 (slot -1), then replayed for several steps while
+    the static inputs change in place (context lengths grow by one, new q / k / v rows).  Every replay's output,
+    caches and slot_mapping equal those of the same steps run eagerly on a copy of the caches, bit for bit."""
+    rng = np.random.default_rng(93 + real)
+    ctx0 = np.concatenate([rng.integers(512, 4090, size=real), np.zeros(bucket - real, np.int64)])
+    steps = 3
+    case = workloads.decode_case(ctx0 + steps, num_blocks=int(sum(math.ceil((c + steps) / 256) for c in ctx0)) + 2,
+                                 seed=94 + real, max_blocks=16)
+    kc, vc = nan_cache(case), nan_cache(case)
+    gpu_store_history(case, kc, vc)  # history up to the last step's context: every step reads only its own part
+    kc2, vc2 = kc.clone(), vc.clone()
+    bt = i32(case.block_tables)
+    live = torch.from_numpy((ctx0 > 0).astype(np.int32)).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(95)
+    draws = [tuple(torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+                   for shape in ((bucket, 16, 128), (bucket, 8, 128), (bucket, 8, 128))) for _ in range(steps)]
+    ws = torch.empty(max(pkv.attn_decode_workspace_bytes(bucket, 16, 8, 128, 16, 256), 1), dtype=torch.uint8,
+                     device="cuda")
+    # Static buffers of the captured step.
+    q_s, k_s, v_s = (torch.empty_like(x) for x in draws[0])
+    cl_s = i32(ctx0.astype(np.int32))
+    out_s = torch.empty_like(q_s)
+    sm_s = torch.empty(bucket, dtype=torch.int32, device="cuda")
+
+    def captured():
+        pkv.attn_decode_paged_store(q_s, k_s, v_s, kc2, vc2, cl_s, bt, case.scale, out=out_s, workspace=ws,
+                                    slot_mapping_out=sm_s)
+
+    # One eager call first (on throwaway copies of the caches), so nothing is set up during the capture.
+    warm_k, warm_v = kc.clone(), vc.clone()
+    pkv.attn_decode_paged_store(draws[0][0], draws[0][1], draws[0][2], warm_k, warm_v, i32(ctx0.astype(np.int32) + 1),
+                                bt, case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    del warm_k, warm_v
+    # Capture with the first step's inputs in place (capturing launches nothing).
+    q_s.copy_(draws[0][0]); k_s.copy_(draws[0][1]); v_s.copy_(draws[0][2])
+    cl_s.add_(live)
+    torch.cuda.synchronize()
+    g = _graph(captured)
+    cl_s.sub_(live)
+    cl = i32(ctx0.astype(np.int32))
+    for step in range(steps):
+        q, k, v = draws[step]
+        cl.add_(live)                        # eager: each real row's context grows by its new token
+        want = pkv.attn_decode_paged_store(q, k, v, kc, vc, cl, bt, case.scale)
+        want_sm = pkv.kv_slot_mapping(bt, 256, bucket, context_lens=cl)
+        q_s.copy_(q); k_s.copy_(k); v_s.copy_(v)
+        cl_s.add_(live)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_s, want), f"step {step}: replayed output differs"
+        assert torch.equal(sm_s, want_sm), f"step {step}: slot_mapping differs"
+        assert torch.equal(kc2.view(torch.int16), kc.view(torch.int16)), f"step {step}: k cache differs"
+        assert torch.equal(vc2.view(torch.int16), vc.view(torch.int16)), f"step {step}: v cache differs"
+        assert bool((out_s[real:] == 0).all()), "padding rows must be zero"
+        assert bool((sm_s[real:] == -1).all()), "padding rows have no slot"
+    log(f"graph decode loop: {real} rows padded to {bucket}, {steps} replays equal the eager steps")
