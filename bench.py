@@ -284,6 +284,47 @@ def bench_decode_latency(pkv, torch, reps):
     return res
 
 
+def bench_sublayer(pkv, torch, steps, warmup):
+    """The synthetic-weight attention sub-layer (qkv GEMM, QK-Norm + RoPE + store, paged attention, o GEMM):
+    a prefill step over workload 3's sequences and a decode step over workload 2's batch."""
+    import numpy as np
+    import workloads
+    sub = pkv.AttentionSublayer(seed=11)
+    res = {}
+    # Prefill: workload 3's lengths, keys read back from the paged cache.
+    c3 = workloads.workload3(device="cuda")
+    n = int(c3.cu_seqlens_q[-1])
+    shape = (c3.num_blocks, c3.block_size, c3.num_kv_heads, c3.head_dim)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    x = torch.randn(n, sub.hidden, generator=gen, device="cuda").to(torch.bfloat16)
+    cu = torch.from_numpy(c3.cu_seqlens_q).cuda()
+    pos = torch.from_numpy(np.concatenate([np.arange(int(L)) for L in c3.Lq]).astype(np.int32)).cuda()
+    bt = torch.from_numpy(c3.block_tables).cuda()
+    mq = int(c3.Lq.max())
+    sm = pkv.kv_slot_mapping(bt, c3.block_size, n, cu_seqlens_q=cu, cu_seqlens_k=cu)
+    pre_ms = run_steps(torch, lambda i: sub.prefill(x, pos, cu, cu, mq, mq, bt, kc, vc, slot_mapping=sm), steps, warmup)
+    res["prefill_workload3"] = {"tokens": n, "ms_per_step": round(pre_ms, 4),
+                                "tokens_per_s": round(n / (pre_ms * 1e-3), 0)}
+    del kc, vc, c3
+    # Decode: workload 2's batch and contexts over caches holding (random) history.
+    c2 = workloads.workload2(device="cuda")
+    kc, vc = build_caches(pkv, torch, c2)
+    bt = torch.from_numpy(c2.block_tables).cuda()
+    cl = torch.from_numpy(c2.context_lens).cuda()
+    xd = torch.randn(c2.batch, sub.hidden, generator=gen, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(max(pkv.attn_decode_workspace_bytes(c2.batch, 16, 8, 128, c2.max_blocks, 256), 1),
+                     dtype=torch.uint8, device="cuda")
+    dec_ms = run_steps(torch, lambda i: sub.decode(xd, cl, bt, kc, vc, workspace=ws), steps, warmup)
+    res["decode_workload2"] = {"batch": c2.batch, "ms_per_step": round(dec_ms, 4),
+                               "kv_GBps": round(int(c2.Lk.astype(int).sum()) * 4096 / (dec_ms * 1e-3) / 1e9, 1)}
+    del kc, vc, c2
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_qknorm_rope_store(pkv, torch, make, steps, warmup, layers):
     """The fused QK-Norm + RoPE + store over one prefill step's new tokens (workload 3's q, k, v)."""
     cases, _ = dev_case_layers(make, layers, torch)
@@ -366,7 +407,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope", "unfused_decode",
-                                       "decode_latency"],
+                                       "decode_latency", "sublayer"],
                     default=None,
                     help="run just one secondary workload (after the headline), e.g. for a profiler")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -397,7 +438,7 @@ def main():
     secondary = {}
     if not args.headline_only:
         want = lambda name: args.only in (None, name)
-        p3 = p4 = st = d5 = qr = fd = dl = None
+        p3 = p4 = st = d5 = qr = fd = dl = sb = None
         if want("unfused_decode"):
             log("unfused decode step (slot_mapping, store, decode), workload 2")
             fd = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers)
@@ -416,6 +457,9 @@ def main():
         if want("decode_latency"):
             log("decode step latency at padded fixed batch sizes, eager and graph")
             dl = bench_decode_latency(pkv, torch, max(args.steps, 20))
+        if want("sublayer"):
+            log("synthetic-weight attention sub-layer, workloads 3 (prefill) and 2 (decode)")
+            sb = bench_sublayer(pkv, torch, args.steps, args.warmup)
         if want("long_decode"):
             log("long padded decode, workload 5")
             d5 = bench_decode(pkv, torch, workloads.workload5_decode, max(args.steps // 5, 3), 2, 2)
@@ -447,6 +491,8 @@ def main():
                                                        "tokens": qr["tokens"]}
         if dl is not None:
             secondary["decode_step_latency_padded_batches"] = dl
+        if sb is not None:
+            secondary["attention_sublayer"] = sb
         if d5 is not None:
             gbs5 = d5["kv_bytes"] / (d5["kernel_ms"] * 1e-3) / 1e9
             secondary["long_decode_workload5"] = {"value": round(gbs5, 1), "unit": "GB/s",

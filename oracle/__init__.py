@@ -30,6 +30,7 @@ from .bf16 import bf16_bits_to_f64, as_f64
 from .slots import slot_mapping_block_walk, slot_mapping_ref, decode_slot_ref
 from .store import store_ref, scatter_rows_ref
 from .qknorm_rope import rms_norm_ref, rope_ref, qk_norm_rope_ref
+from .sublayer import project_split_ref, sublayer_step_ref
 from .attention import (
     kv_head_of,
     attention_ref,
@@ -50,6 +51,8 @@ __all__ = [
     "rms_norm_ref",
     "rope_ref",
     "qk_norm_rope_ref",
+    "project_split_ref",
+    "sublayer_step_ref",
     "kv_head_of",
     "attention_ref",
     "decode_ref",

@@ -27,6 +27,7 @@ from ._lib import (
     attn_decode_paged,
     attn_decode_paged_store,
 )
+from .sublayer import AttentionSublayer
 
 __all__ = [
     "PKV_F32",
@@ -42,4 +43,5 @@ __all__ = [
     "attn_decode_workspace_bytes",
     "attn_decode_paged",
     "attn_decode_paged_store",
+    "AttentionSublayer",
 ]
