@@ -163,15 +163,21 @@ decode_lean_kernel(DecodeKernelArgs p) {
       s_cu[i + 1] = c;
       acc += c;
     }
-    chunk[tid] = acc;
-    __syncthreads();
-    for (int off = 1; off < nt; off <<= 1) {
-      const int64_t y = tid >= off ? chunk[tid - off] : 0;
-      __syncthreads();
-      chunk[tid] += y;
-      __syncthreads();
+    // Exclusive prefix of the chunk sums: an inclusive scan inside each wave (lane shuffles), then the totals of
+    // the preceding waves (one barrier).
+    const int lane = tid & 63, wv = tid >> 6;
+    int64_t inc = acc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int src = lane >= off ? lane - off : lane;
+      const uint32_t lo = __builtin_amdgcn_ds_bpermute(src << 2, int(uint32_t(uint64_t(inc))));
+      const uint32_t hi = __builtin_amdgcn_ds_bpermute(src << 2, int(uint32_t(uint64_t(inc) >> 32)));
+      if (lane >= off) inc += int64_t((uint64_t(hi) << 32) | lo);
     }
-    acc = tid > 0 ? chunk[tid - 1] : 0;
+    if (lane == 63) chunk[wv] = inc;
+    __syncthreads();
+    acc = inc - acc;
+    for (int v = 0; v < wv; ++v) acc += chunk[v];
     for (int i = c0; i < c1; ++i) {
       acc += s_cu[i + 1];
       s_cu[i + 1] = acc;
@@ -416,51 +422,60 @@ decode_lean_kernel(DecodeKernelArgs p) {
   }
 }
 
-// One work-group of 128 threads per (query head, sequence): merge the partial states of the workers whose
-// ranges cut the sequence, or write zeros for an empty context.  Partials are read 8 at a time (independent
-// loads in flight) and merged with a running maximum, the same exact rescaling as everywhere else.
-__global__ void __launch_bounds__(HD) decode_combine_kernel(DecodeKernelArgs p) {
-  const int qh = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// One work-group per sequence: merge, for every query head, the partial states of the workers whose ranges
+// cut the sequence, or write zeros for an empty context.  Thread t takes dims 2 (t mod 64) and 2 (t mod 64) + 1
+// of query heads t / 64, t / 64 + blockDim / 64, ...; partials are read 8 at a time (independent loads in
+// flight) and merged with a running maximum, the same exact rescaling as everywhere else.
+__global__ void __launch_bounds__(1024) decode_combine_kernel(DecodeKernelArgs p) {
+  const int b = blockIdx.x;
   const int64_t T = p.cu[p.batch];
   const int64_t x0 = p.cu[b], x1 = p.cu[b + 1];
-  uint16_t* o = p.out + (int64_t(b) * p.num_q_heads + qh) * HD + d;
-  if (x1 <= x0) {  // padding row or empty context: zeros
-    *o = 0;
-    return;
-  }
   const int W = active_workers(T, p.workers);
-  const int w0 = worker_of(T, W, x0), w1 = worker_of(T, W, x1 - 1);
-  if (w0 == w1) return;  // written by its worker
-  const bool dense = T >= W;  // then no range is empty
-  float M = -INFINITY, L = 0.f, A = 0.f;
-  for (int c0 = w0; c0 <= w1; c0 += 8) {
-    float mv[8], lv[8], av[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int w = c0 + j;
-      const bool valid = w <= w1 && (dense || range_begin(T, W, w) < range_begin(T, W, w + 1));
-      const int64_t row = int64_t(w + b) * p.num_q_heads + qh;
-      const float2 ml = valid ? *reinterpret_cast<const float2*>(p.ws_ml + 2 * row) : make_float2(-INFINITY, 0.f);
-      mv[j] = ml.x;
-      lv[j] = ml.y;
-      av[j] = valid ? p.ws_acc[row * HD + d] : 0.f;
+  const int w0 = x1 > x0 ? worker_of(T, W, x0) : 0, w1 = x1 > x0 ? worker_of(T, W, x1 - 1) : 0;
+  if (x1 > x0 && w0 == w1) return;  // written by its worker
+  const bool dense = T >= W;        // then no range is empty
+  const int pair = threadIdx.x & 63;
+  for (int qh = threadIdx.x >> 6; qh < p.num_q_heads; qh += blockDim.x >> 6) {
+    uint32_t* o = reinterpret_cast<uint32_t*>(p.out + (int64_t(b) * p.num_q_heads + qh) * HD) + pair;
+    if (x1 <= x0) {  // padding row or empty context: zeros
+      *o = 0u;
+      continue;
     }
-    float cm = mv[0];
+    float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
+    for (int c0 = w0; c0 <= w1; c0 += 8) {
+      float mv[8], lv[8], a0[8], a1[8];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) cm = fmaxf(cm, mv[j]);
-    const float mn = fmaxf(M, cm);
-    const float sc = fast_exp2(M - mn);
-    L *= sc;
-    A *= sc;
+      for (int j = 0; j < 8; ++j) {
+        const int w = c0 + j;
+        const bool valid = w <= w1 && (dense || range_begin(T, W, w) < range_begin(T, W, w + 1));
+        const int64_t row = int64_t(w + b) * p.num_q_heads + qh;
+        const float2 ml = valid ? *reinterpret_cast<const float2*>(p.ws_ml + 2 * row) : make_float2(-INFINITY, 0.f);
+        const float2 av = valid ? *reinterpret_cast<const float2*>(p.ws_acc + row * HD + 2 * pair) : make_float2(0.f, 0.f);
+        mv[j] = ml.x;
+        lv[j] = ml.y;
+        a0[j] = av.x;
+        a1[j] = av.y;
+      }
+      float cm = mv[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float e = fast_exp2(mv[j] - mn);
-      L = fmaf(lv[j], e, L);
-      A = fmaf(av[j], e, A);
+      for (int j = 1; j < 8; ++j) cm = fmaxf(cm, mv[j]);
+      const float mn = fmaxf(M, cm);
+      const float sc = fast_exp2(M - mn);
+      L *= sc;
+      A0 *= sc;
+      A1 *= sc;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e = fast_exp2(mv[j] - mn);
+        L = fmaf(lv[j], e, L);
+        A0 = fmaf(a0[j], e, A0);
+        A1 = fmaf(a1[j], e, A1);
+      }
+      M = mn;
     }
-    M = mn;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *o = pack_bf16x2(A0 * inv, A1 * inv);
   }
-  *o = f32_to_bf16(L > 0.f ? A / L : 0.f);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -523,7 +538,7 @@ hipError_t launch_g(DecodeKernelArgs& p, hipStream_t stream) {
   if (!cu_in_lds) hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, p);
   const size_t lds = cu_in_lds ? size_t(p.batch + 1 + threads) * sizeof(int64_t) : 0;
   hipLaunchKernelGGL((decode_lean_kernel<G, STORE>), dim3(head_groups, p.workers), dim3(threads), lds, stream, p);
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.num_q_heads, p.batch), dim3(HD), 0, stream, p);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch), dim3(64 * std::min(16, p.num_q_heads)), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -127,6 +127,17 @@ def test_decode_batch_beyond_lds_prefix_staging(pkv):
     assert bool((out[torch.from_numpy(zeros).cuda()] == 0).all())
 
 
+@pytest.mark.parametrize("ctx", [[20000], [127, 1, 3], [129]])
+def test_decode_one_long_sequence_many_pieces(pkv, ctx):
+    """One sequence cut into as many ranges as the launch has workers (hundreds of partial states merged), and
+    batches with fewer keys than a worker's minimum (one worker takes everything)."""
+    case = workloads.decode_case(ctx, num_blocks=sum(math.ceil(c / 256) for c in ctx) + 2, seed=71,
+                                 max_blocks=max(math.ceil(c / 256) for c in ctx))
+    log(f"decode ctx={ctx}")
+    out, kc, vc, sm = _run_step(pkv, case, paged=True)
+    _check_attention(case, out)
+
+
 PREFILL_CASES = [
     # (dtype, hq, hkv, hd, bs, new lengths, cached prefix lengths, seed)
     ("bf16", 16, 8, 128, 256, [1, 63, 64, 65, 200, 333], [0] * 6, 21),

@@ -82,6 +82,7 @@ CASES = [
     ("bf16", 16, 8, 128, 4, [1, 2, 0], 208),           # fewer keys than workers
     ("f32", 4, 2, 16, 4, [1, 7, 30, 100], 209),        # the tiny fp32 layer's shape
     ("f32", 16, 8, 128, 256, [300, 1], 210),
+    ("bf16", 16, 8, 128, 256, [20000], 212),       # one sequence over every worker: hundreds of pieces
 ]
 
 
