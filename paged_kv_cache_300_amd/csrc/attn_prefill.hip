@@ -47,9 +47,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 #ifndef PKV_PREFILL_H2
 #define PKV_PREFILL_H2 2  // query heads per wave for GQA groups of 2
 #endif
-#ifndef PKV_PREFILL_PP
-#define PKV_PREFILL_PP 1  // GQA groups of 2 on the ping-pong kernels
-#endif
 constexpr float kMinusBig = -1e30f;
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights up to 2^8 before the output is rescaled
 
@@ -476,6 +473,297 @@ __device__ __forceinline__ void attend_tiles(const PrefillKernelArgs& p, const S
   for (int kt = kt_mask; kt < kt1; ++kt) tile_step(std::integral_constant<bool, true>(), kt);
 }
 
+// ----------------------------------------------------------------------------------------------------------
+// Software-pipelined form of attend_tiles, used for the paged cache: while the matrix core forms the scores
+// of key tile j + 1, the vector unit takes the exponentials of tile j (the two interleaved in issue order,
+// since a wave issues in order); while it forms O += P_j V_j, the vector unit masks and reduces the maxima of
+// tile j + 1.  One wave thus keeps both units busy without relying on the other wave of its SIMD being out of
+// phase.  K runs one tile ahead of V in LDS: iteration j reads K_{j+1} and V_j, and stages K_{j+2} and V_{j+1}
+// (two buffers each, one barrier per tile).  Measured on prefix-cache batches (16 sequences, prefixes of
+// 256-4096 and chunks of 64-512 keys, block size 256): +8-10 % over attend_tiles for GQA groups of 2 with the
+// longest-first list, +10 % for groups of 1, +18 % for groups of 4.  On this step's contiguous rows the gain
+// and loss by shape were within +-4 %, so that mode keeps attend_tiles.
+template <int MODE, int CH, bool IS_V>
+__device__ __forceinline__ void load_half(const PrefillKernelArgs& p, const TileSource& s, int kt, int blk,
+                                          u32x4 (&r)[CH]) {
+  const int64_t stride = IS_V ? s.vstride : s.kstride;
+  const uint16_t* head = IS_V ? s.vhead : s.khead;
+  int rows = min(s.Lk - kt * BN, BN);
+  const uint16_t* base;
+  if constexpr (MODE == LOAD_PAGED) {
+    blk = __builtin_amdgcn_readfirstlane(blk);
+    base = head + (int64_t(blk) * p.bs + ((kt * BN) & (p.bs - 1))) * stride;
+  } else {
+    const int64_t row0 = s.k_start + int64_t(kt) * BN;
+    rows = row0 < 0 ? 0 : int(min(int64_t(rows), p.num_k_rows - row0));
+    base = head + row0 * stride;
+  }
+  rows = __builtin_amdgcn_readfirstlane(max(rows, 0));
+  // One resource per row group i (base at row 16 i, size = its valid rows): every lane keeps one offset.
+  constexpr int RSTEP = 64 / CH;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(base + int64_t(RSTEP * i) * stride, uint32_t(max(rows - RSTEP * i, 0)) * uint32_t(stride) * 2u);
+    r[i] = buffer_load16(rs, IS_V ? s.voff[0] : s.koff[0]);
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ void store_half(const u32x4 (&r)[CH], uint16_t* l, int tid) {
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    *reinterpret_cast<u32x4*>(&l[((tid >> 4) + (64 / CH) * i) * KROW + (tid & 15) * 8]) = r[i];
+}
+
+template <int H>
+__device__ __forceinline__ void scores(const uint16_t* lk, const u32x4 (&qreg)[H][4], int col, int grp,
+                                       f32x4_t (&s)[4][H]) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int n = 0; n < H; ++n) s[kb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&lk[(kb * 16 + col) * KROW + ks * 32 + grp * 8]);
+#pragma unroll
+      for (int n = 0; n < H; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
+    }
+}
+
+// Keys kt*64 + 16 kb + 4 grp + r past `lim` get -inf.
+template <int H>
+__device__ __forceinline__ void mask_scores(f32x4_t (&s)[4][H], int room) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool vis = kb * 16 + r <= room;
+#pragma unroll
+      for (int n = 0; n < H; ++n) s[kb][n][r] = vis ? s[kb][n][r] : -INFINITY;
+    }
+}
+
+// Row maxima (scaled by c) over the tile, for every lane of the query's column.
+template <int H>
+__device__ __forceinline__ void tile_max(const f32x4_t (&s)[4][H], float c, float (&mxc)[H]) {
+#pragma unroll
+  for (int n = 0; n < H; ++n) {
+    float m4[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      m4[kb] = fmax_ieee(fmax_ieee(s[kb][n][0], s[kb][n][1]), fmax_ieee(s[kb][n][2], s[kb][n][3]));
+    mxc[n] = max_xor32(max_xor16(fmax_ieee(fmax_ieee(m4[0], m4[1]), fmax_ieee(m4[2], m4[3])))) * c;
+  }
+}
+
+template <int G, int H, int MODE>
+__device__ __forceinline__ void attend_tiles_swp(const PrefillKernelArgs& p, const SeqGeom& g, int b, int kvh, int t,
+                                                 int kt1, uint16_t (*lds_k)[BN * KROW],
+                                                 uint16_t (*lds_v)[BN * VROW], f32x4_t (&o)[8][H],
+                                                 f32x4_t (&o_l)[H], float (&m)[H]) {
+  static_assert(MODE != LOAD_ROWS, "row-wise loads use attend_tiles");
+  constexpr int NT = 64 * TOKEN_WAVES * (G / H);
+  constexpr int CH = 1024 / NT;
+  const int Lq = g.Lq, Lk = g.Lk, q_start = g.q_start;
+  const int t0 = t * BM;
+  const int qpos0 = Lk - Lq + t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int tok = t0 + (wave % TOKEN_WAVES) * 16 + col;
+  const int hb = (wave / TOKEN_WAVES) * H;
+  const int qpos = Lk - Lq + tok;
+
+#pragma unroll
+  for (int n = 0; n < H; ++n) {
+    m[n] = kMinusBig;
+    o_l[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if ((p.causal ? min(Lk, qpos0 + BM) : Lk) <= 0) return;
+
+  const float c = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
+  const uint32_t sign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  u32x4 qreg[H][4];
+  {
+    const bool ok = tok < Lq && q_start + tok < p.num_q_tokens;
+    const uint16_t* qrow = p.q + int64_t(q_start + tok) * p.q_stride + (int64_t(kvh) * G + hb) * HD + grp * 8;
+#pragma unroll
+    for (int n = 0; n < H; ++n)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qrow + n * HD + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+        x.x ^= sign; x.y ^= sign; x.z ^= sign; x.w ^= sign;
+        qreg[n][ks] = x;
+      }
+  }
+  TileSource src;
+  src.khead = p.k + int64_t(kvh) * HD;
+  src.vhead = p.v + int64_t(kvh) * HD;
+  src.bt_row = p.bt ? p.bt + int64_t(b) * p.max_blocks : nullptr;
+  src.krow = tid >> 4;
+  src.Lk = Lk;
+  src.k_start = g.k_start;
+  src.kstride = p.bt ? int64_t(p.num_kv_heads) * HD : p.k_stride;
+  src.vstride = p.bt ? int64_t(p.num_kv_heads) * HD : p.v_stride;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    src.koff[i] = uint32_t(((src.krow + (64 / CH) * i) * src.kstride + (tid & 15) * 8) * 2);
+    src.voff[i] = uint32_t(((src.krow + (64 / CH) * i) * src.vstride + (tid & 15) * 8) * 2);
+  }
+  auto tile_block = [&](int kt) { return MODE == LOAD_PAGED ? block_of(p, src.bt_row, (kt * BN) >> p.bs_shift) : 0; };
+  const uint32_t one2 = col == 0 ? 0x3F803F80u : 0u;
+  const u32x4 ones = u32x4{one2, one2, one2, one2};
+  const int lim = p.causal ? min(qpos, Lk - 1) : Lk - 1;
+  int kt_mask = Lk / BN;
+  if (p.causal) kt_mask = min(kt_mask, qpos0 + 1 > 0 ? (qpos0 + 1) / BN : 0);
+
+  // Prologue: K_0, V_0 and K_1 staged; scores and maxima of tile 0.
+  u32x4 kst[CH], vst[CH];
+  {
+    const int blk0 = tile_block(0);
+    load_half<MODE, CH, false>(p, src, 0, blk0, kst);
+    load_half<MODE, CH, true>(p, src, 0, blk0, vst);
+    store_half<CH>(kst, lds_k[0], tid);
+    store_half<CH>(vst, lds_v[0], tid);
+    if (kt1 > 1) {
+      load_half<MODE, CH, false>(p, src, 1, tile_block(1), kst);
+      store_half<CH>(kst, lds_k[1], tid);
+    }
+  }
+  __syncthreads();
+  f32x4_t sc[4][H];
+  scores<H>(lds_k[0], qreg, col, grp, sc);
+  if (0 >= kt_mask) mask_scores<H>(sc, lim - grp * 4);
+  {
+    float mxc[H];
+    tile_max<H>(sc, c, mxc);
+#pragma unroll
+    for (int n = 0; n < H; ++n) m[n] = fmaxf(m[n], mxc[n]);
+  }
+  if (kt1 > 1) __syncthreads();  // every wave's reads of K_0 are done before K_2 replaces it
+
+  // Weights of the scores in sc (reference m), packed as the P^T operands of the two 32-key halves.
+  auto weights = [&](u32x4 (&pb)[2][H]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int n = 0; n < H; ++n) {
+        float e[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = fast_exp2(fmaf(sc[2 * h][n][r], c, -m[n]));
+          e[4 + r] = fast_exp2(fmaf(sc[2 * h + 1][n][r], c, -m[n]));
+        }
+        pb[h][n] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                         pack_bf16x2(e[6], e[7])};
+      }
+  };
+  // O += P V over tile kt (V in lds_v[kt & 1]); o_l accumulates the normaliser as in attend_tiles.
+  auto accumulate = [&](const u32x4 (&pb)[2][H], int kt) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = h * 32 + grp * 4 + (col >> 2);
+      const uint16_t* vrow = &lds_v[kt & 1][row * VROW + (col & 3) * 4];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const u32x2 lo = ds_read_tr16(vrow + d * 16);
+        const u32x2 hi = ds_read_tr16(vrow + 16 * VROW + d * 16);
+        const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int n = 0; n < H; ++n) o[d][n] = mfma_16x16x32(a, pb[h][n], o[d][n]);
+      }
+#pragma unroll
+      for (int n = 0; n < H; ++n) o_l[n] = mfma_16x16x32(ones, pb[h][n], o_l[n]);
+    }
+  };
+
+  // Steady state: tile kt + 1 exists.  Loads past the last tile (K_{kt+2} near the end) have zero valid rows:
+  // they read nothing and stage zeros into a buffer no one reads.  MASKED: tile kt + 1 needs the mask.
+  const int last_lb = p.bt ? p.max_blocks - 1 : 0;
+  auto step = [&](auto masked_tag, int kt) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int blk2 = MODE == LOAD_PAGED ? block_of(p, src.bt_row, min(((kt + 2) * BN) >> p.bs_shift, last_lb)) : 0;
+    load_half<MODE, CH, false>(p, src, kt + 2, blk2, kst);
+    // A: scores of tile kt + 1 on the matrix core, weights of tile kt on the vector unit.
+    f32x4_t sn[4][H];
+    u32x4 pb[2][H];
+    // Sixteen groups, each: the H products of one (ks, kb) K fragment, then 8 H / 16 pairs of weights, in that
+    // issue order (scheduling barriers between groups); K fragments are read two groups ahead.
+    {
+      const uint16_t* lk = lds_k[(kt + 1) & 1];
+      auto kfrag = [&](int i) {
+        return *reinterpret_cast<const u32x4*>(&lk[((i & 3) * 16 + col) * KROW + (i >> 2) * 32 + grp * 8]);
+      };
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int n = 0; n < H; ++n) sn[kb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      u32x4 kf[3];
+      kf[0] = kfrag(0);
+      kf[1] = kfrag(1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + 2 < 16) kf[(i + 2) % 3] = kfrag(i + 2);
+#pragma unroll
+        for (int n = 0; n < H; ++n) sn[i & 3][n] = mfma_16x16x32(kf[i % 3], qreg[n][i >> 2], sn[i & 3][n]);
+#pragma unroll
+        for (int cidx = i * H / 2; cidx < (i + 1) * H / 2; ++cidx) {
+          const int h = cidx / (4 * H), n = (cidx / 4) % H, j = cidx % 4;
+          const int kbs = 2 * h + (j >> 1), r0 = (j & 1) * 2;
+          const float e0 = fast_exp2(fmaf(sc[kbs][n][r0], c, -m[n]));
+          const float e1 = fast_exp2(fmaf(sc[kbs][n][r0 + 1], c, -m[n]));
+          pb[h][n][j] = pack_bf16x2(e0, e1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // K_{kt+2} replaces K_kt (last read in the previous tile); V_{kt+1} is fetched now and replaces V_{kt-1}
+    // (also read in the previous tile), so each staging set is live for half a tile only.
+    store_half<CH>(kst, lds_k[kt & 1], tid);
+    load_half<MODE, CH, true>(p, src, kt + 1, tile_block(kt + 1), vst);
+    // B: O += P V of tile kt on the matrix core, mask and maxima of tile kt + 1 on the vector unit.
+    if constexpr (MASKED) mask_scores<H>(sn, lim - ((kt + 1) * BN + grp * 4));
+    accumulate(pb, kt);
+    float mxc[H];
+    tile_max<H>(sn, c, mxc);
+    bool need = false;
+#pragma unroll
+    for (int n = 0; n < H; ++n) need |= mxc[n] > m[n] + kRescaleSlack;
+    if (__any(need)) {
+#pragma unroll
+      for (int n = 0; n < H; ++n) {
+        const float mn = fmaxf(m[n], mxc[n]);
+        const float alpha = fast_exp2(m[n] - mn);
+        m[n] = mn;
+        o_l[n] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[d][n] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int n = 0; n < H; ++n) sc[kb][n] = sn[kb][n];
+    store_half<CH>(vst, lds_v[(kt + 1) & 1], tid);
+    __syncthreads();
+  };
+  // Tile kt + 1 needs no mask while kt + 1 < kt_mask.
+  const int split = min(max(kt_mask - 1, 0), kt1 - 1);
+  for (int kt = 0; kt < split; ++kt) step(std::integral_constant<bool, false>(), kt);
+  for (int kt = split; kt < kt1 - 1; ++kt) step(std::integral_constant<bool, true>(), kt);
+  // Last tile: weights and O += P V only.
+  {
+    u32x4 pb[2][H];
+    weights(pb);
+    accumulate(pb, kt1 - 1);
+    __syncthreads();
+  }
+}
+
 // Normalise and write: lane holds dims 16 d + 4 grp + r of query `tok`, head kvh*G + hb + n.
 template <int G, int H>
 __device__ __forceinline__ void write_output(const PrefillKernelArgs& p, const SeqGeom& g, int kvh, int t,
@@ -518,231 +806,11 @@ __global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2) prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * VROW];
   f32x4_t o[8][H], o_l[H];
   float m[H];
-  attend_tiles<G, H, MODE>(p, g, b, kvh, t, 0, unit_tiles(g, t), lds_k, lds_v, o, o_l, m);
+  if constexpr (MODE == LOAD_PAGED)
+    attend_tiles_swp<G, H, MODE>(p, g, b, kvh, t, unit_tiles(g, t), lds_k, lds_v, o, o_l, m);
+  else
+    attend_tiles<G, H, MODE>(p, g, b, kvh, t, 0, unit_tiles(g, t), lds_k, lds_v, o, o_l, m);
   write_output<G, H>(p, g, kvh, t, o, o_l);
-}
-
-// ----------------------------------------------------------------------------------------------------------
-// Ping-pong form for GQA groups of 2: a work-group of 8 waves takes 128 query tokens (two 64-token halves, A
-// and B, 4 waves each) of one kv head, both of its query heads per wave, sharing every K/V tile.  A key tile's
-// work per half is a matrix phase (O^T += V^T P^T for the previous tile, then S^T = K Q^T for this one) and a
-// vector phase (mask, maximum, rescale, exponentials, P packed to bf16).  Half B runs one phase behind half A
-// and a barrier ends every phase, so on each SIMD one wave is in its matrix phase while the other is in its
-// vector phase: the matrix cores and the vector units work at the same time instead of taking turns.  Tiles
-// are triple-buffered in LDS (a tile is read during four consecutive phases); all 8 waves stage the next tile
-// at the start of every other phase.
-constexpr int PP_WAVES = 8;
-constexpr int PP_NT = 64 * PP_WAVES;
-constexpr int PP_CH = 1024 / PP_NT;  // 16-byte chunks per thread per K (and per V) tile
-constexpr int PP_BUF = 3;
-
-template <int MODE>
-__device__ __forceinline__ void attend_pp(const PrefillKernelArgs& p, const SeqGeom& g, int b, int kvh, int t2,
-                                          uint16_t (*lds_k)[BN * KROW], uint16_t (*lds_v)[BN * VROW],
-                                          f32x4_t (&o)[8][2], f32x4_t (&o_l)[2]) {
-  constexpr int G = 2, H = 2;
-  const int Lq = g.Lq, Lk = g.Lk, q_start = g.q_start;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = wave >> 2;                      // 0: A (tokens 0-63 of the pair), 1: B (64-127)
-  const int t64 = 2 * t2 + half;                   // this half's 64-token query tile
-  const int col = lane & 15, grp = lane >> 4;
-  const int tok = t64 * BM + (wave & 3) * 16 + col;
-  const int qpos = Lk - Lq + tok;
-  const int qpos0 = Lk - Lq + t64 * BM;
-  // Key tiles of each half (none for a half past the sequence's rows) and the tiles to stage.
-  const int ntA = unit_tiles(g, 2 * t2);
-  const int ntB = 2 * t2 + 1 < g.T ? unit_tiles(g, 2 * t2 + 1) : 0;
-  const int nt = half ? ntB : ntA;
-  const int nt_all = max(ntA, ntB);
-
-  float m[H];
-#pragma unroll
-  for (int n = 0; n < H; ++n) {
-    m[n] = kMinusBig;
-    o_l[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  if (Lk <= 0) return;  // no key at all (uniform over the work-group): zero output
-
-  const float c = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
-  const uint32_t sign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-  u32x4 qreg[H][4];
-  {
-    const bool ok = tok < Lq && q_start + tok < p.num_q_tokens;
-    const uint16_t* qrow = p.q + int64_t(q_start + tok) * p.q_stride + int64_t(kvh) * G * HD + grp * 8;
-#pragma unroll
-    for (int n = 0; n < H; ++n)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qrow + n * HD + ks * 32) : u32x4{0u, 0u, 0u, 0u};
-        x.x ^= sign; x.y ^= sign; x.z ^= sign; x.w ^= sign;
-        qreg[n][ks] = x;
-      }
-  }
-
-  TileSource src;
-  src.khead = p.k + int64_t(kvh) * HD;
-  src.vhead = p.v + int64_t(kvh) * HD;
-  src.bt_row = p.bt ? p.bt + int64_t(b) * p.max_blocks : nullptr;
-  src.krow = tid >> 4;
-  src.Lk = Lk;
-  src.k_start = g.k_start;
-  src.kstride = p.bt ? int64_t(p.num_kv_heads) * HD : p.k_stride;
-  src.vstride = p.bt ? int64_t(p.num_kv_heads) * HD : p.v_stride;
-#pragma unroll
-  for (int i = 0; i < PP_CH; ++i) {
-    src.koff[i] = uint32_t(((src.krow + (64 / PP_CH) * i) * src.kstride + (tid & 15) * 8) * 2);
-    src.voff[i] = uint32_t(((src.krow + (64 / PP_CH) * i) * src.vstride + (tid & 15) * 8) * 2);
-  }
-  auto tile_block = [&](int kt) { return MODE == LOAD_PAGED ? block_of(p, src.bt_row, (kt * BN) >> p.bs_shift) : 0; };
-
-  const uint32_t one2 = col == 0 ? 0x3F803F80u : 0u;
-  const u32x4 ones = u32x4{one2, one2, one2, one2};
-  const int lim = p.causal ? min(qpos, Lk - 1) : Lk - 1;
-  int kt_mask = Lk / BN;  // this half's tiles from kt_mask on need a mask
-  if (p.causal) kt_mask = min(kt_mask, qpos0 + 1 > 0 ? (qpos0 + 1) / BN : 0);
-
-  // Prologue: tile 0 into buffer 0, tile 1 staged in registers.
-  Staged<PP_CH> st = load_tile<MODE, PP_CH>(p, src, 0, tile_block(0));
-  store_tile(st, lds_k[0], lds_v[0], tid);
-  if (nt_all > 1) st = load_tile<MODE, PP_CH>(p, src, 1, tile_block(1));
-  __syncthreads();
-
-  f32x4_t s[4][H];
-  u32x4 pb[2][H];  // P of the previous tile, bf16, one u32x4 per 32-key half and head
-  const int slots = 2 * nt_all + 2;
-  for (int k = 0; k < slots; ++k) {
-    if ((k & 1) == 0) {  // stage: tile k/2 + 1 into LDS, tile k/2 + 2 into registers
-      const int j1 = (k >> 1) + 1;
-      if (j1 < nt_all) {
-        store_tile(st, lds_k[j1 % PP_BUF], lds_v[j1 % PP_BUF], tid);
-        if (j1 + 1 < nt_all) st = load_tile<MODE, PP_CH>(p, src, j1 + 1, tile_block(j1 + 1));
-      }
-    }
-    const int kk = k - half;  // half B runs one phase behind
-    if (kk >= 0 && (kk & 1) == 0) {
-      // Matrix phase j: O^T += V^T P^T for tile j - 1, then S^T = K Q^T for tile j.
-      const int j = kk >> 1;
-      __builtin_amdgcn_s_setprio(1);
-      if (j >= 1 && j - 1 < nt) {
-        const int vb = (j - 1) % PP_BUF;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int row = h2 * 32 + grp * 4 + (col >> 2);
-          const uint16_t* vrow = &lds_v[vb][row * VROW + (col & 3) * 4];
-#pragma unroll
-          for (int d = 0; d < 8; ++d) {
-            const u32x2 lo = ds_read_tr16(vrow + d * 16);
-            const u32x2 hi = ds_read_tr16(vrow + 16 * VROW + d * 16);
-            const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-            for (int n = 0; n < H; ++n) o[d][n] = mfma_16x16x32(a, pb[h2][n], o[d][n]);
-          }
-#pragma unroll
-          for (int n = 0; n < H; ++n) o_l[n] = mfma_16x16x32(ones, pb[h2][n], o_l[n]);
-        }
-      }
-      if (j < nt) {
-        const int kbuf = j % PP_BUF;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int n = 0; n < H; ++n) s[kb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(&lds_k[kbuf][(kb * 16 + col) * KROW + ks * 32 + grp * 8]);
-#pragma unroll
-            for (int n = 0; n < H; ++n) s[kb][n] = mfma_16x16x32(a, qreg[n][ks], s[kb][n]);
-          }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    } else if (kk >= 0) {
-      // Vector phase j: mask, maximum, rescale when the reference moves, exponentials, P to bf16.
-      const int j = kk >> 1;
-      if (j < nt) {
-        if (j >= kt_mask) {
-          const int room = lim - (j * BN + grp * 4);
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const bool vis = kb * 16 + r <= room;
-#pragma unroll
-              for (int n = 0; n < H; ++n) s[kb][n][r] = vis ? s[kb][n][r] : -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < H; ++n) {
-          float m4[4];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            m4[kb] = fmax_ieee(fmax_ieee(s[kb][n][0], s[kb][n][1]), fmax_ieee(s[kb][n][2], s[kb][n][3]));
-          const float mxc = max_xor32(max_xor16(fmax_ieee(fmax_ieee(m4[0], m4[1]), fmax_ieee(m4[2], m4[3])))) * c;
-          if (mxc > m[n] + kRescaleSlack) {  // rare after the first tile: move the reference, rescale O and l
-            const float alpha = fast_exp2(m[n] - mxc);
-            m[n] = mxc;
-            o_l[n] *= alpha;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) o[d][n] *= alpha;
-          }
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            float e[8];
-#pragma unroll
-            for (int q8 = 0; q8 < 8; ++q8) e[q8] = fast_exp2(fmaf(s[2 * h2 + (q8 >> 2)][n][q8 & 3], c, -m[n]));
-            pb[h2][n] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                              pack_bf16x2(e[6], e[7])};
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-template <int MODE>
-__device__ __forceinline__ void pp_unit(const PrefillKernelArgs& p, int b, int kvh, int t2) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[PP_BUF][BN * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[PP_BUF][BN * VROW];
-  const SeqGeom g = seq_geom(p, b);
-  f32x4_t o[8][2], o_l[2];
-  attend_pp<MODE>(p, g, b, kvh, t2, lds_k, lds_v, o, o_l);
-  // write_output's lane map with the pair's two 64-token tiles: wave w of half w / 4 writes tile 2 t2 + w / 4.
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int tok = (2 * t2 + (wave >> 2)) * BM + (wave & 3) * 16 + col;
-  float inv[2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const float lt = __int_as_float(__builtin_amdgcn_ds_bpermute(col << 2, __float_as_int(o_l[n][0])));
-    inv[n] = lt > 0.f ? 1.f / lt : 0.f;
-  }
-  if (tok < g.Lq && g.q_start + tok < p.num_q_tokens) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      uint16_t* orow = p.out + (int64_t(g.q_start + tok) * p.num_q_heads + kvh * 2 + n) * HD + grp * 4;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        u32x2 w;
-        w.x = pack_bf16x2(o[d][n][0] * inv[n], o[d][n][1] * inv[n]);
-        w.y = pack_bf16x2(o[d][n][2] * inv[n], o[d][n][3] * inv[n]);
-        *reinterpret_cast<u32x2*>(orow + d * 16) = w;
-      }
-    }
-  }
-}
-
-// Grid form: one work-group per (kv head, sequence, pair of query tiles), latest pair first.
-template <int MODE>
-__global__ void __launch_bounds__(PP_NT, 1) prefill_pp_kernel(PrefillKernelArgs p) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int t2 = (p.max_tiles + 1) / 2 - 1 - int(blockIdx.z);
-  const int T = (max(p.cu_q[b + 1] - p.cu_q[b], 0) + BM - 1) / BM;
-  if (2 * t2 >= T) return;
-  pp_unit<MODE>(p, b, kvh, t2);
 }
 
 // Longest-first order.  When the work of a query tile is not given by its index (cached prefixes of different
@@ -757,7 +825,6 @@ constexpr size_t PLAN_HEADER_BYTES = 256;
 
 struct PlanArgs {
   int batch;
-  int pair;      // 1: units are pairs of query tiles (the ping-pong kernels), 0: single tiles
   int buckets;   // key-tile counts 1 .. buckets (larger counts share the last), from max_seqlen_k
   int unit_cap;  // list capacity; units past it are dropped (the host sizes it from num_q_tokens)
   int2* list;    // [unit_cap] (sequence, query tile), longest first
@@ -792,15 +859,14 @@ __device__ int block_exclusive_scan(int* a, int n, int* chunk) {
 
 __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(PrefillKernelArgs p, PlanArgs pa) {
   __shared__ int uoff[PLAN_MAX_BATCH + 1];  // first unit of each sequence
-  __shared__ int sc0[PLAN_MAX_BATCH], snk[PLAN_MAX_BATCH], sT[PLAN_MAX_BATCH];
+  __shared__ int sc0[PLAN_MAX_BATCH], snk[PLAN_MAX_BATCH];
   __shared__ int start[PLAN_BUCKETS];       // bucket i holds units with `buckets` - i key tiles (clamped)
   __shared__ int chunk[PLAN_THREADS];
   const int tid = threadIdx.x, nb = pa.batch, nbk = pa.buckets;
   for (int b = tid; b < nb; b += PLAN_THREADS) {
     const SeqGeom g = seq_geom(p, b);
     const int T = min(g.T, p.max_tiles);  // rows past max_seqlen_q are not computed
-    uoff[b] = pa.pair ? (T + 1) >> 1 : T;
-    sT[b] = T;
+    uoff[b] = T;
     sc0[b] = g.c0;
     snk[b] = g.NKe;
   }
@@ -818,8 +884,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(PrefillKerne
     }
     b = lo;
     t = u - uoff[lo];
-    const int tl = pa.pair ? min(2 * t + 1, sT[lo] - 1) : t;  // a pair's work is its later tile's
-    const int nk = min(max(tl + 1 + sc0[lo], 1), snk[lo]);
+    const int nk = min(max(t + 1 + sc0[lo], 1), snk[lo]);
     return nbk - min(nk, nbk);
   };
   for (int u = tid; u < units; u += PLAN_THREADS) {
@@ -848,31 +913,11 @@ __global__ void __launch_bounds__(64 * TOKEN_WAVES * (G / H), 2)
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][BN * VROW];
   f32x4_t o[8][H], o_l[H];
   float m[H];
-  attend_tiles<G, H, MODE>(p, g, u.x, kvh, u.y, 0, unit_tiles(g, u.y), lds_k, lds_v, o, o_l, m);
+  if constexpr (MODE == LOAD_PAGED)
+    attend_tiles_swp<G, H, MODE>(p, g, u.x, kvh, u.y, unit_tiles(g, u.y), lds_k, lds_v, o, o_l, m);
+  else
+    attend_tiles<G, H, MODE>(p, g, u.x, kvh, u.y, 0, unit_tiles(g, u.y), lds_k, lds_v, o, o_l, m);
   write_output<G, H>(p, g, kvh, u.y, o, o_l);
-}
-
-template <int MODE>
-__global__ void __launch_bounds__(PP_NT, 1)
-    prefill_pp_ordered_kernel(PrefillKernelArgs p, const int2* list, const int* count) {
-  const int kvh = int(blockIdx.x % unsigned(p.num_kv_heads));
-  const int rank = int(blockIdx.x / unsigned(p.num_kv_heads));
-  if (rank >= *count) return;
-  const int2 u = list[rank];
-  pp_unit<MODE>(p, u.x, kvh, u.y);
-}
-
-// GQA groups of 2 reading a paged cache on the ping-pong kernels.
-hipError_t launch_pp(const PrefillKernelArgs& p, int batch, const PlanArgs* plan, hipStream_t stream) {
-  if (plan) {
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, p, *plan);
-    hipLaunchKernelGGL((prefill_pp_ordered_kernel<LOAD_PAGED>), dim3(unsigned(plan->unit_cap) * unsigned(p.num_kv_heads)),
-                       dim3(PP_NT), 0, stream, p, plan->list, plan->count);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((prefill_pp_kernel<LOAD_PAGED>), dim3(p.num_kv_heads, batch, (p.max_tiles + 1) / 2), dim3(PP_NT),
-                     0, stream, p);
-  return hipGetLastError();
 }
 
 template <int G, int H>
@@ -983,14 +1028,6 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, void* workspace, size_t worksp
     planp = &plan;
   } else if (p.max_tiles > 65535) {
     return hipErrorInvalidConfiguration;
-  }
-  // Ping-pong kernels for GQA groups of 2 reading a paged cache (prefix-cache / chunked prefill: long key
-  // ranges for every query tile; measured +4-5 % on workload 4).  For causal self-attention over the step's
-  // own rows the 128-token units cost more on the diagonal and in the tail than the overlap gains (-11 % on
-  // workload 3), so those keep the 64-token kernels.
-  if (group == 2 && PKV_PREFILL_PP && mode == LOAD_PAGED) {
-    if (planp) plan.pair = 1;
-    return launch_pp(p, a.batch, planp, stream);
   }
   return group == 1   ? launch_g<1, 1>(p, a.batch, mode, planp, stream)
          : group == 2 ? launch_g<2, PKV_PREFILL_H2>(p, a.batch, mode, planp, stream)

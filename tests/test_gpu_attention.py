@@ -177,6 +177,10 @@ ORDER_CASES = [
     (8, 8, [200, 900], [1200, 0], 64, 74),
     (32, 8, [400, 129], [2000, 77], 128, 75),
     (16, 8, [100, 37], [500, 900], 7, 76),
+    # keys that fill the block-table row exactly (the pipelined paged loop looks a tile past the last one)
+    (16, 8, [256, 64], [768, 0], 256, 77),
+    (32, 8, [128, 1], [128, 63], 64, 78),
+    (8, 8, [64], [0], 64, 79),
 ]
 
 
