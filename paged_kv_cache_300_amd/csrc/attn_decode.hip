@@ -422,10 +422,12 @@ decode_lean_kernel(DecodeKernelArgs p) {
   }
 }
 
-// One work-group per sequence: merge, for every query head, the partial states of the workers whose ranges
+// One work-group per (sequence, pair of query heads): merge the partial states of the workers whose ranges
 // cut the sequence, or write zeros for an empty context.  Thread t takes dims 2 (t mod 64) and 2 (t mod 64) + 1
-// of query heads t / 64, t / 64 + blockDim / 64, ...; partials are read 8 at a time (independent loads in
-// flight) and merged with a running maximum, the same exact rescaling as everywhere else.
+// of query head blockIdx.y * blockDim / 64 + t / 64 (then in steps of gridDim.y * blockDim / 64); partials are
+// read 8 at a time (independent loads in flight) and merged with a running maximum, the same exact rescaling
+// as everywhere else.  Two heads per work-group measured about 1 % faster on the whole decode call than one
+// work-group per sequence over all 16 heads (more work-groups start at once; 1, 2 or 4 heads are alike).
 __global__ void __launch_bounds__(1024) decode_combine_kernel(DecodeKernelArgs p) {
   const int b = blockIdx.x;
   const int64_t T = p.cu[p.batch];
@@ -435,7 +437,7 @@ __global__ void __launch_bounds__(1024) decode_combine_kernel(DecodeKernelArgs p
   if (x1 > x0 && w0 == w1) return;  // written by its worker
   const bool dense = T >= W;        // then no range is empty
   const int pair = threadIdx.x & 63;
-  for (int qh = threadIdx.x >> 6; qh < p.num_q_heads; qh += blockDim.x >> 6) {
+  for (int qh = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6); qh < p.num_q_heads; qh += gridDim.y * (blockDim.x >> 6)) {
     uint32_t* o = reinterpret_cast<uint32_t*>(p.out + (int64_t(b) * p.num_q_heads + qh) * HD) + pair;
     if (x1 <= x0) {  // padding row or empty context: zeros
       *o = 0u;
@@ -538,7 +540,7 @@ hipError_t launch_g(DecodeKernelArgs& p, hipStream_t stream) {
   if (!cu_in_lds) hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, p);
   const size_t lds = cu_in_lds ? size_t(p.batch + 1 + threads) * sizeof(int64_t) : 0;
   hipLaunchKernelGGL((decode_lean_kernel<G, STORE>), dim3(head_groups, p.workers), dim3(threads), lds, stream, p);
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch), dim3(64 * std::min(16, p.num_q_heads)), 0, stream, p);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.batch, (p.num_q_heads + 1) / 2), dim3(64 * std::min(2, p.num_q_heads)), 0, stream, p);
   return hipGetLastError();
 }
 
