@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-Headline: one decode layer-step of workload 2 (batch 64, context_lens U[512,4096], block_size 256, bf16,
+Headline: one decode layer-step of the batch-64 decode workload (batch 64, context_lens U[512,4096], block_size 256, bf16,
 16 q / 8 kv heads, head_dim 128): slot_mapping, the store of each sequence's new token and the paged decode
 attention, in one attn_decode_paged_store call (the same results as kv_slot_mapping -> kv_store ->
 attn_decode_paged, which is measured too, under ``secondary``).  ``value`` is the KV-cache bytes the decode
@@ -16,9 +16,9 @@ The same JSON line carries:
                 rocprofv3 counters kept in profiles/ (null if the kernel source changed since they were
                 taken);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, BLAS pinned to one thread;
-  secondary     the unfused decode step and call, varlen prefill TFLOP/s (workload 3), prefix-cache prefill
-                TFLOP/s (workload 4), the store sweep GB/s (workload 5, N=16384), the long padded decode GB/s
-                (workload 5, batch 256) and the fused QK-Norm + RoPE + store GB/s (workload 3's tokens).
+  secondary     the unfused decode step and call, varlen prefill TFLOP/s (8 sequences of 128-2048), prefix-cache
+                prefill TFLOP/s (16 sequences), the store sweep GB/s (N=16384), the long padded decode GB/s
+                (batch 256) and the fused QK-Norm + RoPE + store GB/s (the 8 prefill sequences' tokens).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
 """
@@ -286,13 +286,13 @@ def bench_decode_latency(pkv, torch, reps):
 
 def bench_sublayer(pkv, torch, steps, warmup):
     """The synthetic-weight attention sub-layer (qkv GEMM, QK-Norm + RoPE + store, paged attention, o GEMM):
-    a prefill step over workload 3's sequences and a decode step over workload 2's batch."""
+    a prefill step over the 8 varlen prefill sequences and a decode step over the batch-64 decode workload."""
     import numpy as np
     import workloads
     sub = pkv.AttentionSublayer(seed=11)
     res = {}
-    # Prefill: workload 3's lengths, keys read back from the paged cache.
-    c3 = workloads.workload3(device="cuda")
+    # Prefill: the 8 varlen prefill sequences' lengths, keys read back from the paged cache.
+    c3 = workloads.varlen_prefill_8seq(device="cuda")
     n = int(c3.cu_seqlens_q[-1])
     shape = (c3.num_blocks, c3.block_size, c3.num_kv_heads, c3.head_dim)
     kc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
@@ -306,11 +306,11 @@ def bench_sublayer(pkv, torch, steps, warmup):
     mq = int(c3.Lq.max())
     sm = pkv.kv_slot_mapping(bt, c3.block_size, n, cu_seqlens_q=cu, cu_seqlens_k=cu)
     pre_ms = run_steps(torch, lambda i: sub.prefill(x, pos, cu, cu, mq, mq, bt, kc, vc, slot_mapping=sm), steps, warmup)
-    res["prefill_workload3"] = {"tokens": n, "ms_per_step": round(pre_ms, 4),
+    res["prefill_varlen_8seq"] = {"tokens": n, "ms_per_step": round(pre_ms, 4),
                                 "tokens_per_s": round(n / (pre_ms * 1e-3), 0)}
     del kc, vc, c3
-    # Decode: workload 2's batch and contexts over caches holding (random) history.
-    c2 = workloads.workload2(device="cuda")
+    # Decode: the batch-64 workload's batch and contexts over caches holding (random) history.
+    c2 = workloads.decode_batch64(device="cuda")
     kc, vc = build_caches(pkv, torch, c2)
     bt = torch.from_numpy(c2.block_tables).cuda()
     cl = torch.from_numpy(c2.context_lens).cuda()
@@ -318,7 +318,7 @@ def bench_sublayer(pkv, torch, steps, warmup):
     ws = torch.empty(max(pkv.attn_decode_workspace_bytes(c2.batch, 16, 8, 128, c2.max_blocks, 256), 1),
                      dtype=torch.uint8, device="cuda")
     dec_ms = run_steps(torch, lambda i: sub.decode(xd, cl, bt, kc, vc, workspace=ws), steps, warmup)
-    res["decode_workload2"] = {"batch": c2.batch, "ms_per_step": round(dec_ms, 4),
+    res["decode_batch64"] = {"batch": c2.batch, "ms_per_step": round(dec_ms, 4),
                                "kv_GBps": round(int(c2.Lk.astype(int).sum()) * 4096 / (dec_ms * 1e-3) / 1e9, 1)}
     del kc, vc, c2
     torch.cuda.empty_cache()
@@ -326,7 +326,7 @@ def bench_sublayer(pkv, torch, steps, warmup):
 
 
 def bench_qknorm_rope_store(pkv, torch, make, steps, warmup, layers):
-    """The fused QK-Norm + RoPE + store over one prefill step's new tokens (workload 3's q, k, v)."""
+    """The fused QK-Norm + RoPE + store over one prefill step's new tokens (the 8 varlen prefill sequences' q, k, v)."""
     cases, _ = dev_case_layers(make, layers, torch)
     c0 = cases[0]
     n, hq, hkv, hd = int(c0.cu_seqlens_q[-1]), c0.num_q_heads, c0.num_kv_heads, c0.head_dim
@@ -363,7 +363,7 @@ def bench_qknorm_rope_store(pkv, torch, make, steps, warmup, layers):
 
 def cpu_baseline(min_seconds=10.0, n_seqs=16):
     """The oracle's decode step (slot_mapping, store, attention) on the first ``n_seqs`` sequences of
-    workload 2 (same context lengths, shapes and distributions), repeated until ``min_seconds`` elapsed."""
+    the batch-64 decode workload (same context lengths, shapes and distributions), repeated until ``min_seconds`` elapsed."""
     import numpy as np
     import oracle
     import workloads
@@ -379,7 +379,7 @@ def cpu_baseline(min_seconds=10.0, n_seqs=16):
         reps, secs = _time_oracle_step(case, kc, vc, min_seconds)
     kv_bytes = int(ctx.sum()) * 2 * 8 * 128 * 2
     return {"value": round(kv_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"workload 2's first {n_seqs} sequences (sum ctx {int(ctx.sum())}), full decode step "
+            "sample": f"the batch-64 decode workload's first {n_seqs} sequences (sum ctx {int(ctx.sum())}), full decode step "
                       f"(slot_mapping + store + attention, float64), {reps} repetitions, {secs:.2f} s each"}
 
 
@@ -423,14 +423,14 @@ def main():
     pkv.lib()
     torch.cuda.set_device(0)
 
-    log("decode step (fused store + decode), workload 2")
-    dec = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers, fused=True)
+    log("decode step (fused store + decode), batch 64")
+    dec = bench_decode(pkv, torch, workloads.decode_batch64, args.steps, args.warmup, args.layers, fused=True)
     achieved = dec["kv_bytes"] / (dec["kernel_ms"] * 1e-3) / 1e9
     value = dec["kv_bytes"] / (dec["wall_ms"] * 1e-3) / 1e9
     dec_hash = source_hash("attn_decode.hip", "common.h")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("attn_decode_paged_store_workload2", dec_hash),
+                "traffic": measured_traffic("attn_decode_paged_store_decode_batch64", dec_hash),
                 "kernel": "attn_decode_paged_store (decode_lean_kernel<2, store> + decode_combine_kernel)",
                 "kernel_ms": round(dec["kernel_ms"], 5), "algorithmic_bytes": dec["kv_bytes"],
                 "source_hash": dec_hash}
@@ -440,20 +440,20 @@ def main():
         want = lambda name: args.only in (None, name)
         p3 = p4 = st = d5 = qr = fd = dl = sb = None
         if want("unfused_decode"):
-            log("unfused decode step (slot_mapping, store, decode), workload 2")
-            fd = bench_decode(pkv, torch, workloads.workload2, args.steps, args.warmup, args.layers)
+            log("unfused decode step (slot_mapping, store, decode), batch 64")
+            fd = bench_decode(pkv, torch, workloads.decode_batch64, args.steps, args.warmup, args.layers)
         if want("prefill"):
-            log("prefill, workload 3")
-            p3 = bench_prefill(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers, paged=False)
+            log("varlen prefill, 8 sequences")
+            p3 = bench_prefill(pkv, torch, workloads.varlen_prefill_8seq, args.steps, args.warmup, args.layers, paged=False)
         if want("prefix"):
-            log("prefix prefill, workload 4")
-            p4 = bench_prefill(pkv, torch, workloads.workload4, args.steps, args.warmup, args.layers, paged=True)
+            log("prefix prefill, 16 sequences")
+            p4 = bench_prefill(pkv, torch, workloads.prefix_prefill_16seq, args.steps, args.warmup, args.layers, paged=True)
         if want("store"):
-            log("store sweep, workload 5")
+            log("store sweep, 16384 tokens")
             st = bench_store(pkv, torch, args.steps, args.warmup)
         if want("qknorm_rope"):
-            log("QK-Norm + RoPE + store, workload 3's tokens")
-            qr = bench_qknorm_rope_store(pkv, torch, workloads.workload3, args.steps, args.warmup, args.layers)
+            log("QK-Norm + RoPE + store, the 8 prefill sequences' tokens")
+            qr = bench_qknorm_rope_store(pkv, torch, workloads.varlen_prefill_8seq, args.steps, args.warmup, args.layers)
         if want("decode_latency"):
             log("decode step latency at padded fixed batch sizes, eager and graph")
             dl = bench_decode_latency(pkv, torch, max(args.steps, 20))
@@ -461,9 +461,9 @@ def main():
             log("synthetic-weight attention sub-layer, workloads 3 (prefill) and 2 (decode)")
             sb = bench_sublayer(pkv, torch, args.steps, args.warmup)
         if want("long_decode"):
-            log("long padded decode, workload 5")
-            d5 = bench_decode(pkv, torch, workloads.workload5_decode, max(args.steps // 5, 3), 2, 2)
-        for name, r in (("varlen_prefill_workload3", p3), ("prefix_prefill_workload4", p4)):
+            log("long padded decode, batch 256")
+            d5 = bench_decode(pkv, torch, workloads.long_decode_batch256, max(args.steps // 5, 3), 2, 2)
+        for name, r in (("varlen_prefill_8seq", p3), ("prefix_prefill_16seq", p4)):
             if r is None:
                 continue
             tf = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
@@ -472,20 +472,20 @@ def main():
                                "step_ms": round(r["wall_ms"], 4), "flops": r["flops"], "tokens": r["tokens"]}
         if st is not None:
             gbs = st["bytes"] / (st["kernel_ms"] * 1e-3) / 1e9
-            secondary["store_sweep_workload5"] = {"value": round(gbs, 1), "unit": "GB/s",
+            secondary["store_sweep_16k"] = {"value": round(gbs, 1), "unit": "GB/s",
                                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                                  "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
                                                  "tokens": st["tokens"]}
         if fd is not None:
             gbk = fd["kv_bytes"] / (fd["kernel_ms"] * 1e-3) / 1e9
-            secondary["decode_step_unfused_workload2"] = {
+            secondary["decode_step_unfused_batch64"] = {
                 "value": round(fd["kv_bytes"] / (fd["wall_ms"] * 1e-3) / 1e9, 1), "unit": "GB/s",
                 "step_ms": round(fd["wall_ms"], 5), "call_ms": round(fd["kernel_ms"], 5),
                 "call_GBps": round(gbk, 1), "call_frac_hbm_peak": round(gbk / HBM_PEAK_GBS, 4),
                 "step": "kv_slot_mapping + kv_store + attn_decode_paged (call = attn_decode_paged alone)"}
         if qr is not None:
             gbq = qr["bytes"] / (qr["kernel_ms"] * 1e-3) / 1e9
-            secondary["qknorm_rope_store_workload3"] = {"value": round(gbq, 1), "unit": "GB/s",
+            secondary["qknorm_rope_store_8seq_tokens"] = {"value": round(gbq, 1), "unit": "GB/s",
                                                        "frac_hbm_peak": round(gbq / HBM_PEAK_GBS, 4),
                                                        "kernel_ms": round(qr["kernel_ms"], 5), "bytes": qr["bytes"],
                                                        "tokens": qr["tokens"]}
@@ -495,7 +495,7 @@ def main():
             secondary["attention_sublayer"] = sb
         if d5 is not None:
             gbs5 = d5["kv_bytes"] / (d5["kernel_ms"] * 1e-3) / 1e9
-            secondary["long_decode_workload5"] = {"value": round(gbs5, 1), "unit": "GB/s",
+            secondary["long_decode_batch256"] = {"value": round(gbs5, 1), "unit": "GB/s",
                                                  "frac_hbm_peak": round(gbs5 / HBM_PEAK_GBS, 4),
                                                  "kernel_ms": round(d5["kernel_ms"], 4), "kv_bytes": d5["kv_bytes"],
                                                  "step_ms": round(d5["wall_ms"], 4)}
@@ -518,7 +518,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workloads.WORKLOADS[2], "batch": dec["batch"], "sum_context_lens": dec["sum_ctx"],
+        "config": {"workload": workloads.WORKLOADS["decode_batch64"], "batch": dec["batch"], "sum_context_lens": dec["sum_ctx"],
                    "heads": "16 q / 8 kv", "head_dim": 128, "block_size": 256, "layers_rotated": args.layers,
                    "step": "attn_decode_paged_store (slot_mapping + store of the new token + paged decode)"},
         "roofline": roofline,

@@ -12,7 +12,7 @@ seven steps; §4 "QK-Norm 与 RoPE"]:
   ``store.store_ref``; the page's integration check compares the cache's k rows with the normalised and
   rotated k [P2 §7].
 
-Readings (listed in DESIGN.md):
+Readings where the page leaves a step open:
 
 * RoPE's formula is left to another lesson; the plain reading is the rotary embedding of RoFormer in the
   "rotate half" layout: element i of a head is paired with element i + head_dim/2 and the pair is rotated

@@ -58,10 +58,10 @@ def _check_attention(case, out, rows=None):
     return worst
 
 
-def test_workload1_tiny_fp32_end_to_end(pkv):
-    """Workload 1: store + causal prefill (contiguous and paged), then one decode step per sequence."""
-    pre = workloads.workload1()
-    log(f"workload 1 block_tables={pre.block_tables.tolist()}")
+def test_tiny_fp32_layer_end_to_end(pkv):
+    """Tiny fp32 layer: store + causal prefill (contiguous and paged), then one decode step per sequence."""
+    pre = workloads.tiny_fp32_prefill()
+    log(f"tiny fp32 layer block_tables={pre.block_tables.tolist()}")
     for paged in (False, True):
         out, kc, vc, sm = _run_step(pkv, pre, paged)
         np.testing.assert_array_equal(to_host(sm), oracle_slot_mapping(pre))
@@ -72,7 +72,7 @@ def test_workload1_tiny_fp32_end_to_end(pkv):
     assert np.array_equal(to_host(kc).view(np.uint32), want_k.view(np.uint32))
     assert np.array_equal(to_host(vc).view(np.uint32), want_v.view(np.uint32))
     # decode step on top of the same cache
-    dec = workloads.workload1_decode(pre)
+    dec = workloads.tiny_fp32_decode(pre)
     sm_d = gpu_slot_mapping(dec)
     want_sm = oracle_slot_mapping(dec)
     np.testing.assert_array_equal(to_host(sm_d), want_sm)

@@ -111,10 +111,10 @@ def test_ranges_that_start_at_the_new_token(pkv, batch, ctx_len):
     _check_oracle(case, out, rows=list(range(0, batch, 37)) + [batch - 1])
 
 
-def test_workload2_decode_shape(pkv):
-    """Workload 2 (batch 64, context lengths U[512, 4096], 4096-block cache): sampled rows against the oracle."""
-    case = workloads.workload2()
-    log(f"fused decode, workload 2: sum ctx {int(case.Lk.sum())}")
+def test_decode_batch64_shape(pkv):
+    """Batch-64 decode workload (batch 64, context lengths U[512, 4096], 4096-block cache): sampled rows against the oracle."""
+    case = workloads.decode_batch64()
+    log(f"fused decode, batch 64: sum ctx {int(case.Lk.sum())}")
     out, _ = _both(pkv, case)
     _check_oracle(case, out, rows=[0, 17, 40, 63])
 

@@ -77,9 +77,9 @@ def _check_attention(case, out, seqs):
     assert worst <= BF16_TOL
 
 
-def test_workload2_decode_full(pkv):
-    case = workloads.workload2(device="cuda")
-    log(f"workload 2: batch {case.batch}, sum ctx {int(case.Lk.sum())}")
+def test_decode_batch64_full(pkv):
+    case = workloads.decode_batch64(device="cuda")
+    log(f"decode batch 64: batch {case.batch}, sum ctx {int(case.Lk.sum())}")
     out, kc, vc, sm = _step(pkv, case, paged=True)
     sm_h = to_host(sm)
     np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
@@ -87,9 +87,9 @@ def test_workload2_decode_full(pkv):
     _check_attention(case, out, range(case.batch))
 
 
-def test_workload3_varlen_prefill_full(pkv):
-    case = workloads.workload3(device="cuda")
-    log(f"workload 3: lengths {case.Lq.tolist()}")
+def test_varlen_prefill_8seq_full(pkv):
+    case = workloads.varlen_prefill_8seq(device="cuda")
+    log(f"varlen prefill: lengths {case.Lq.tolist()}")
     out, kc, vc, sm = _step(pkv, case, paged=False)
     sm_h = to_host(sm)
     np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
@@ -97,9 +97,9 @@ def test_workload3_varlen_prefill_full(pkv):
     _check_attention(case, out, range(case.batch))
 
 
-def test_workload4_prefix_prefill_full(pkv):
-    case = workloads.workload4(device="cuda")
-    log(f"workload 4: new {case.Lq.tolist()} total {case.Lk.tolist()}")
+def test_prefix_prefill_16seq_full(pkv):
+    case = workloads.prefix_prefill_16seq(device="cuda")
+    log(f"prefix prefill: new {case.Lq.tolist()} total {case.Lk.tolist()}")
     out, kc, vc, sm = _step(pkv, case, paged=True)
     sm_h = to_host(sm)
     np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
@@ -107,10 +107,10 @@ def test_workload4_prefix_prefill_full(pkv):
     _check_attention(case, out, range(case.batch))
 
 
-def test_workload5_padded_long_decode(pkv):
-    case = workloads.workload5_decode(device="cuda")
+def test_long_decode_batch256_padded(pkv):
+    case = workloads.long_decode_batch256(device="cuda")
     real = np.where(case.Lk > 0)[0]
-    log(f"workload 5 decode: {len(real)} real rows, sum ctx {int(case.Lk.sum())}")
+    log(f"long padded decode: {len(real)} real rows, sum ctx {int(case.Lk.sum())}")
     out, kc, vc, sm = _step(pkv, case, paged=True)
     sm_h = to_host(sm)
     np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
@@ -124,7 +124,7 @@ def test_workload5_padded_long_decode(pkv):
     assert bool((out[224:] == 0).all())  # padding rows
 
 
-def test_workload5_store_sweep_bit_exact(pkv):
+def test_store_sweep_16k_bit_exact(pkv):
     sweep = workloads.store_sweep(device="cuda")
     shape = (sweep.num_blocks, sweep.block_size, sweep.num_kv_heads, sweep.head_dim)
     d = sweep.num_kv_heads * sweep.head_dim

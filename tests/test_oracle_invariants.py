@@ -222,10 +222,10 @@ def test_split_merge_equals_whole(seed):
     np.testing.assert_allclose(o2, (w @ v) / w.sum(), rtol=1e-12, atol=1e-14)
 
 
-def test_workload1_end_to_end_consistency():
-    """Workload 1 through the oracle: store, prefill and decode agree with the contiguous definition."""
-    pre = workloads.workload1()
-    dec = workloads.workload1_decode(pre)
+def test_tiny_fp32_layer_end_to_end_consistency():
+    """The tiny fp32 layer through the oracle: store, prefill and decode agree with the contiguous definition."""
+    pre = workloads.tiny_fp32_prefill()
+    dec = workloads.tiny_fp32_decode(pre)
     cache = workloads.nan_cache_host(pre.num_blocks, pre.block_size, 2, 16, "f32")
     sm = oracle.slot_mapping_ref(pre.block_tables, pre.block_size, 9, cu_seqlens_q=pre.cu_seqlens_q)
     kc, vc = oracle.store_ref(pre.k, pre.v, cache, cache, sm)

@@ -27,19 +27,20 @@ import numpy as np
 
 NAN_BITS = {"bf16": 0x7FC0, "f32": 0x7FC00000}
 
-# The five workloads (shapes of the Qwen3-0.6B attention layer: 16 q heads, 8 kv heads, head_dim 128,
-# block_size 256, unless stated).
+# The workloads, named by what they are (shapes of the Qwen3-0.6B attention layer: 16 q heads, 8 kv heads,
+# head_dim 128, block_size 256, unless stated).
 WORKLOADS = {
-    1: "tiny fp32 layer: 2 seqs of 6 and 3 tokens, block_size 4, 8 blocks, 4/2 heads, head_dim 16; "
-       "store + causal prefill, then one decode step per sequence",
-    2: "decode: batch 64, context_lens U[512,4096], block_size 256, 4096-block cache, bf16 16/8/128; "
-       "store one token per sequence then paged decode",
-    3: "varlen causal prefill: 8 seqs, lengths U[128,2048], bf16 16/8/128, block_size 256; "
-       "store all tokens then contiguous attention",
-    4: "prefix-cache / chunked prefill: 16 seqs, cached prefix U[256,4096] + new chunk U[64,512], "
-       "K/V read through block_tables, bf16 16/8/128",
-    5: "padded long decode: batch 256 (last 32 rows padding, slot -1), context_lens U[1024,32768], "
-       "bf16 16/8/128; plus a store sweep of 16384 tokens into distinct random slots",
+    "tiny_fp32": "tiny fp32 layer: 2 seqs of 6 and 3 tokens, block_size 4, 8 blocks, 4/2 heads, head_dim 16; "
+                 "store + causal prefill, then one decode step per sequence",
+    "decode_batch64": "decode: batch 64, context_lens U[512,4096], block_size 256, 4096-block cache, "
+                      "bf16 16/8/128; store one token per sequence then paged decode",
+    "varlen_prefill_8seq": "varlen causal prefill: 8 seqs, lengths U[128,2048], bf16 16/8/128, block_size 256; "
+                           "store all tokens then contiguous attention",
+    "prefix_prefill_16seq": "prefix-cache / chunked prefill: 16 seqs, cached prefix U[256,4096] + new chunk "
+                            "U[64,512], K/V read through block_tables, bf16 16/8/128",
+    "long_decode_batch256": "padded long decode: batch 256 (last 32 rows padding, slot -1), context_lens "
+                            "U[1024,32768], bf16 16/8/128; plus a store sweep of 16384 tokens into distinct "
+                            "random slots",
 }
 
 
@@ -153,8 +154,8 @@ def make_case(Lq, Lk, *, num_q_heads, num_kv_heads, head_dim, block_size, num_bl
                   decode=False, max_blocks=max_blocks, rng=rng, scale=scale)
 
 
-def workload1(device="cpu", seed=1):
-    """Workload 1, prefill part: two prompts of 6 and 3 tokens, fp32, block_size 4, 8 blocks.
+def tiny_fp32_prefill(device="cpu", seed=1):
+    """Tiny fp32 layer, prefill part: two prompts of 6 and 3 tokens, fp32, block_size 4, 8 blocks.
 
     The block tables come from ``permutation(8)``: sequence 0 takes two blocks, sequence 1 one block.
     """
@@ -162,8 +163,8 @@ def workload1(device="cpu", seed=1):
                      num_blocks=8, dtype="f32", seed=seed, device=device, scale=0.25)
 
 
-def workload1_decode(prefill, device="cpu", seed=101):
-    """Workload 1, decode part: one new token per sequence after ``prefill`` (context 7 and 4).
+def tiny_fp32_decode(prefill, device="cpu", seed=101):
+    """Tiny fp32 layer, decode part: one new token per sequence after ``prefill`` (context 7 and 4).
 
     The sequences keep the blocks of the prefill step (7 tokens still fit in 2 blocks of 4, 4 in 1).
     The history is exactly the prefill step's keys and values.
@@ -200,20 +201,20 @@ def decode_case(context_lens, *, num_q_heads=16, num_kv_heads=8, head_dim=128, b
                   device=device, decode=True, max_blocks=max_blocks, rng=rng, scale=scale)
 
 
-def workload2(device="cpu", seed=2):
+def decode_batch64(device="cpu", seed=2):
     rng = np.random.default_rng(seed)
     ctx = rng.integers(512, 4096, size=64, endpoint=True)
     return decode_case(ctx, num_blocks=4096, seed=seed, device=device, max_blocks=16, rng=rng)
 
 
-def workload3(device="cpu", seed=3):
+def varlen_prefill_8seq(device="cpu", seed=3):
     rng = np.random.default_rng(seed)
     lens = rng.integers(128, 2048, size=8, endpoint=True)
     return make_case(lens, lens, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
                      num_blocks=1024, dtype="bf16", seed=seed, device=device, rng=rng)
 
 
-def workload4(device="cpu", seed=4):
+def prefix_prefill_16seq(device="cpu", seed=4):
     rng = np.random.default_rng(seed)
     prefix = rng.integers(256, 4096, size=16, endpoint=True)
     chunk = rng.integers(64, 512, size=16, endpoint=True)
@@ -221,7 +222,7 @@ def workload4(device="cpu", seed=4):
                      num_blocks=4096, dtype="bf16", seed=seed, device=device, max_blocks=18, rng=rng)
 
 
-def workload5_decode(device="cpu", seed=5):
+def long_decode_batch256(device="cpu", seed=5):
     """224 real rows followed by 32 padding rows (context 0, slot -1, block row all -1)."""
     rng = np.random.default_rng(seed)
     ctx = np.concatenate([rng.integers(1024, 32768, size=224, endpoint=True), np.zeros(32, np.int64)])
