@@ -55,7 +55,7 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = -1, /* a null pointer, a negative size, inconsistent shapes or strides */
-  PKV_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement (e.g. head_dim > 256) */
+  PKV_ERR_UNSUPPORTED = -2, /* a valid request the library does not implement (e.g. head_dim > 256) */
   PKV_ERR_WORKSPACE = -3,   /* a workspace smaller than its size function requires (or missing for decode) */
   PKV_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
 };
