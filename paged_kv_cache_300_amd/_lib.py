@@ -103,6 +103,10 @@ def _rows(t, name, heads=None):
     """[tokens, heads, head_dim] with head_dim contiguous and heads packed; returns the token stride."""
     if t.dim() != 3:
         raise ValueError(f"{name} must be [tokens, heads, head_dim]")
+    if t.numel() == 0:  # no rows: strides carry no meaning (an empty view may report zeros)
+        if heads is not None and t.shape[1] != heads:
+            raise ValueError(f"{name} has {t.shape[1]} heads, expected {heads}")
+        return t.shape[1] * t.shape[2]
     if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
         raise ValueError(f"{name} needs stride(-1) == 1 and stride(1) == head_dim")
     if heads is not None and t.shape[1] != heads:

@@ -146,3 +146,20 @@ def test_workspace_size_formula_is_monotone():
     a = L.attn_prefill_workspace_bytes(16, 5000, 512, 16, 8, 128, pkv.PKV_BF16)
     b = L.attn_prefill_workspace_bytes(16, 9000, 512, 16, 8, 128, pkv.PKV_BF16)
     assert 0 < a <= b
+
+
+def test_row_tensor_checks_on_host():
+    """Token-row tensors: head_dim contiguous and heads packed; an empty batch passes whatever strides its view
+    reports (a zero-row view of a NumPy array reports zeros)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_300_amd import _lib as L
+    empty = torch.from_numpy(np.zeros((0, 8, 128), np.int16)).view(torch.bfloat16)
+    assert L._rows(empty, "k", heads=8) == 8 * 128
+    with pytest.raises(ValueError):
+        L._rows(empty, "k", heads=4)
+    full = torch.zeros(5, 8, 128, dtype=torch.bfloat16)
+    assert L._rows(full, "k") == 8 * 128
+    assert L._rows(torch.zeros(5, 24, 128)[:, 8:16], "k") == 24 * 128  # a view into a merged projection
+    with pytest.raises(ValueError):
+        L._rows(full.transpose(1, 2), "k")
