@@ -34,6 +34,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "launch.h"
@@ -497,30 +498,32 @@ Layout workspace_layout(int batch, int num_q_heads) {
 }
 
 // W: as many work-groups as the device keeps resident at once (cached per device and kernel shape).
+// The caches are atomics: several host threads may launch at once (they store equal values).
 int resident_workers(const void* kernel, int threads, int key) {
-  static int cached[64][6][MAX_WAVES + 1] = {};
+  static std::atomic<int> cached[64][6][MAX_WAVES + 1] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int& slot = cached[dev][key][threads / 64];
-  if (slot > 0) return slot;
+  std::atomic<int>& slot = cached[dev][key][threads / 64];
+  if (const int v = slot.load(std::memory_order_relaxed); v > 0) return v;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads,
                                                    (LDS_CU_MAX + 64 * MAX_WAVES) * sizeof(int64_t)) !=
           hipSuccess || per_cu <= 0)
     per_cu = 1;
-  slot = std::min(MAX_WORKERS, cus * per_cu);
-  return slot;
+  const int v = std::min(MAX_WORKERS, cus * per_cu);
+  slot.store(v, std::memory_order_relaxed);
+  return v;
 }
 
 int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] > 0) return cached[dev];
+  if (const int v = cached[dev].load(std::memory_order_relaxed); v > 0) return v;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  cached[dev] = cus;
+  cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
