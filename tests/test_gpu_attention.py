@@ -152,12 +152,14 @@ PREFILL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("order", [True, False])
-@pytest.mark.parametrize("paged", [False, True])
-@pytest.mark.parametrize("dtype,hq,hkv,hd,bs,lq,prefix,seed", PREFILL_CASES)
+# Contiguous K/V (paged=False) only for cases without a cached prefix: a prefix is only readable through the
+# block tables.
+PREFILL_RUNS = [(*c, paged, order) for c in PREFILL_CASES for paged in (False, True) for order in (True, False)
+                if paged or not any(c[6])]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,hd,bs,lq,prefix,seed,paged,order", PREFILL_RUNS)
 def test_prefill_small(pkv, dtype, hq, hkv, hd, bs, lq, prefix, seed, paged, order):
-    if not paged and any(prefix):
-        pytest.skip("a cached prefix is only readable through the block tables")
     lk = [a + b for a, b in zip(lq, prefix)]
     num_blocks = sum(math.ceil(c / bs) for c in lk) + 2
     case = workloads.make_case(lq, lk, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, block_size=bs,
