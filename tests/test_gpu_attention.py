@@ -138,6 +138,24 @@ def test_decode_one_long_sequence_many_pieces(pkv, ctx):
     _check_attention(case, out)
 
 
+@pytest.mark.parametrize("batch,paged", [(3000, False), (3000, True), (4100, True)])
+def test_prefill_many_short_sequences(pkv, batch, paged):
+    """Thousands of short sequences (0-5 new tokens, paged: after cached prefixes of 0-99): the longest-first
+    planner up to its 4096-sequence limit, and the grid order beyond it (no workspace is asked for there)."""
+    rng = np.random.default_rng(81 + batch)
+    lq = rng.integers(0, 6, batch)
+    prefix = rng.integers(0, 100, batch) if paged else np.zeros(batch, np.int64)
+    lk = lq + prefix
+    bs = 16
+    case = workloads.make_case(lq, lk, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=bs,
+                               num_blocks=int(sum(math.ceil(c / bs) for c in lk)) + 2, dtype="bf16", seed=81 + batch)
+    assert (pkv.attn_prefill_workspace_bytes(batch, int(lq.sum()), int(lq.max()), 16, 8, 128) > 0) == (batch <= 4096)
+    log(f"prefill batch {batch} paged={paged}, {int(lq.sum())} new tokens")
+    out, kc, vc, sm = _run_step(pkv, case, paged)
+    np.testing.assert_array_equal(to_host(sm), oracle_slot_mapping(case))
+    _check_attention(case, out, rows=list(range(0, batch, 13)) + [batch - 1])
+
+
 PREFILL_CASES = [
     # (dtype, hq, hkv, hd, bs, new lengths, cached prefix lengths, seed)
     ("bf16", 16, 8, 128, 256, [1, 63, 64, 65, 200, 333], [0] * 6, 21),
