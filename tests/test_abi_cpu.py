@@ -4,6 +4,8 @@ arguments on the host before touching the device (no compute call is made here).
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -163,3 +165,22 @@ def test_row_tensor_checks_on_host():
     assert L._rows(torch.zeros(5, 24, 128)[:, 8:16], "k") == 24 * 128  # a view into a merged projection
     with pytest.raises(ValueError):
         L._rows(full.transpose(1, 2), "k")
+
+
+def test_c_program_uses_the_abi(tmp_path):
+    """The header compiles as C11 and a plain C program links the library and gets the documented host-side
+    results (workspace sizes, rejected arguments with a message); nothing is enqueued on a GPU."""
+    _lib()  # skips when the library is not built
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    here = os.path.dirname(os.path.abspath(__file__))
+    pkg = os.path.join(os.path.dirname(here), "paged_kv_cache_300_amd")
+    exe = str(tmp_path / "abi_from_c")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [gcc, "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.dirname(HEADER)}", f"-I{rocm}/include",
+           os.path.join(here, "c_abi", "abi_from_c.c"), f"-L{pkg}", "-lpagedkv", f"-Wl,-rpath,{pkg}", "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", run.stdout + run.stderr
