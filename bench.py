@@ -230,7 +230,7 @@ def bench_store(pkv, torch, steps, warmup):
     moved = 2 * n * row * 2 + 4 * n  # read + write of K and V rows, plus the slots
     del kc, vc
     torch.cuda.empty_cache()
-    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n}
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n, "sets": len(slots)}
 
 
 def bench_decode_latency(pkv, torch, reps):
@@ -475,7 +475,7 @@ def main():
             secondary["store_sweep_16k"] = {"value": round(gbs, 1), "unit": "GB/s",
                                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                                  "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
-                                                 "tokens": st["tokens"]}
+                                                 "tokens": st["tokens"], "sets_rotated": st["sets"]}
         if fd is not None:
             gbk = fd["kv_bytes"] / (fd["kernel_ms"] * 1e-3) / 1e9
             secondary["decode_step_unfused_batch64"] = {

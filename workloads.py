@@ -241,9 +241,12 @@ class StoreSweep:
     dtype: str
 
 
-def store_sweep(n_tokens=16384, *, n_sets=4, num_blocks=4096, block_size=256, num_kv_heads=8,
+def store_sweep(n_tokens=16384, *, n_sets=8, num_blocks=4096, block_size=256, num_kv_heads=8,
                 head_dim=128, dtype="bf16", seed=5, device="cpu"):
-    """Independent (key, value, slots) sets for the store bandwidth sweep; slots distinct per set."""
+    """Independent (key, value, slots) sets for the store bandwidth sweep; slots distinct per set.
+
+    Eight sets of 64 MiB of K and V rows (512 MiB, twice the GPU's 256 MB last-level cache), used in turn, so no
+    set's rows are still cached when it comes round again: the sweep reads them from HBM."""
     rng = np.random.default_rng(seed)
     num_slots = num_blocks * block_size
     slots = [rng.choice(num_slots, n_tokens, replace=False).astype(np.int32) for _ in range(n_sets)]
