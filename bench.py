@@ -453,7 +453,9 @@ def main():
             st = bench_store(pkv, torch, args.steps, args.warmup)
         if want("qknorm_rope"):
             log("QK-Norm + RoPE + store, the 8 prefill sequences' tokens")
-            qr = bench_qknorm_rope_store(pkv, torch, workloads.varlen_prefill_8seq, args.steps, args.warmup, args.layers)
+            # at least 8 input sets (8 x 67 MB of q, k, v rows, twice the last-level cache): rows are read from HBM
+            qr = bench_qknorm_rope_store(pkv, torch, workloads.varlen_prefill_8seq, args.steps, args.warmup,
+                                         max(args.layers, 8))
         if want("decode_latency"):
             log("decode step latency at padded fixed batch sizes, eager and graph")
             dl = bench_decode_latency(pkv, torch, max(args.steps, 20))
@@ -488,7 +490,7 @@ def main():
             secondary["qknorm_rope_store_8seq_tokens"] = {"value": round(gbq, 1), "unit": "GB/s",
                                                        "frac_hbm_peak": round(gbq / HBM_PEAK_GBS, 4),
                                                        "kernel_ms": round(qr["kernel_ms"], 5), "bytes": qr["bytes"],
-                                                       "tokens": qr["tokens"]}
+                                                       "tokens": qr["tokens"], "sets_rotated": max(args.layers, 8)}
         if dl is not None:
             secondary["decode_step_latency_padded_batches"] = dl
         if sb is not None:
