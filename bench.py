@@ -18,7 +18,9 @@ The same JSON line carries:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, BLAS pinned to one thread;
   secondary     the unfused decode step and call, varlen prefill TFLOP/s (8 sequences of 128-2048), prefix-cache
                 prefill TFLOP/s (16 sequences), the store sweep GB/s (N=16384), the long padded decode GB/s
-                (batch 256) and the fused QK-Norm + RoPE + store GB/s (the 8 prefill sequences' tokens).
+                (batch 256) and the fused QK-Norm + RoPE + store GB/s (the 8 prefill sequences' tokens); the
+                bandwidth-bound ones rotate enough independent inputs (``sets_rotated``) that each call reads
+                from HBM, not from rows the last-level cache kept from an earlier call.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
 """
