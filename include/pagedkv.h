@@ -73,8 +73,12 @@ const char* pkv_last_error(void);
  * Decode mode (context_lens != NULL, both cu_seqlens NULL): row b is position context_lens[b]-1.
  * Output slot_mapping [num_tokens]: rows past the last token (cu_seqlens_q[batch], or batch in decode
  *   mode) are -1, the padding marker kv_store skips [P2 §5.1].  A position below 0, a logical block past
- *   max_blocks_per_seq, or a negative block-table entry also gives -1.
+ *   max_blocks_per_seq, a negative block-table entry, or a slot above INT32_MAX (formed in 64 bits, never
+ *   wrapped) also gives -1.
  * Requires: block_size >= 1; batch >= 0; num_tokens >= 0; cu_seqlens_q nondecreasing from 0 (device).
+ *   The device arrays hold cu_seqlens_q/k [batch+1], context_lens [batch] and block_tables
+ *   [batch, max_blocks_per_seq] entries: their lengths are not visible through these pointers, so a shorter
+ *   array is read past (the Python binding checks the lengths).
  */
 int kv_slot_mapping(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* context_lens,
                     const int32_t* block_tables, int32_t batch, int32_t max_blocks_per_seq,

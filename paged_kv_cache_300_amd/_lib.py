@@ -131,6 +131,15 @@ def kv_slot_mapping(block_tables, block_size, num_tokens, cu_seqlens_q=None, cu_
     if block_tables.dim() != 2:
         raise ValueError("block_tables must be [batch, max_blocks]")
     batch, max_blocks = block_tables.shape
+    # the kernels read cu_seqlens_* [batch + 1] and context_lens [batch]: shorter tensors would be read past
+    if (cu_seqlens_q is None) == (context_lens is None):
+        raise ValueError("give cu_seqlens_q (prefill) or context_lens (decode), not both")
+    if cu_seqlens_q is not None and cu_seqlens_q.numel() != batch + 1:
+        raise ValueError("cu_seqlens_q must have batch + 1 entries (one row of block_tables per sequence)")
+    if cu_seqlens_k is not None and cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("cu_seqlens_k must have batch + 1 entries (one row of block_tables per sequence)")
+    if context_lens is not None and context_lens.numel() != batch:
+        raise ValueError("context_lens must have one entry per row of block_tables")
     if out is None:
         out = torch.empty(num_tokens, dtype=torch.int32, device=block_tables.device)
     _meta(out, "out")

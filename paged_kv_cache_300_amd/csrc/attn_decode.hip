@@ -145,7 +145,8 @@ decode_lean_kernel(DecodeKernelArgs p) {
     for (int i = threadIdx.x; i < p.batch; i += blockDim.x) {
       const int pos = p.ctx[i] - 1, lb = pos >= 0 ? pos / p.bs : 0;
       const int blk = pos >= 0 && lb < p.max_blocks ? p.bt[int64_t(i) * p.max_blocks + lb] : -1;
-      p.slot_out[i] = blk >= 0 ? blk * p.bs + pos % p.bs : -1;
+      const int64_t slot = blk >= 0 ? int64_t(blk) * p.bs + pos % p.bs : -1;  // 64-bit: no wrap into range
+      p.slot_out[i] = slot <= int64_t(INT32_MAX) ? int32_t(slot) : -1;
     }
   }
   // Prefix sums of the clamped context lengths.  Up to LDS_CU_MAX - 1 sequences every work-group scans them

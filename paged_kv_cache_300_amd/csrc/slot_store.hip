@@ -10,13 +10,17 @@
 
 namespace pkv {
 
+// Slot of position p through one block-table row, or -1 when there is none: p < 0, a logical block past the
+// row, a negative entry, or a slot that an int32 slot_mapping cannot hold (the product is formed in 64 bits,
+// so a large block id never wraps into a small slot).
 __device__ __forceinline__ int32_t slot_of_position(const int32_t* bt_row, int max_blocks, int block_size, int p) {
   if (p < 0) return -1;
   const int i = p / block_size;
   if (i >= max_blocks) return -1;
   const int blk = bt_row[i];
   if (blk < 0) return -1;
-  return blk * block_size + p % block_size;
+  const int64_t slot = int64_t(blk) * block_size + p % block_size;
+  return slot <= int64_t(INT32_MAX) ? int32_t(slot) : -1;
 }
 
 // Prefill: token t belongs to the sequence b with cu_q[b] <= t < cu_q[b+1] (binary search); it sits at

@@ -1,7 +1,9 @@
 """Helpers for the GPU parity tests: move seeded host inputs to the device, build caches through the HIP path,
 and build the matching oracle results on the host.  The two sides share only the generator's inputs."""
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -101,21 +103,32 @@ def logical_kv(case, b, which):
     return np.concatenate(parts)
 
 
+def _oracle_one(case, b):
+    lk = int(case.Lk[b])
+    q0, q1 = int(case.cu_seqlens_q[b]), int(case.cu_seqlens_q[b + 1])
+    q = f64(case.q[q0:q1], case.dtype)
+    if lk == 0:
+        return np.zeros_like(q)
+    k = oracle.as_f64(logical_kv(case, b, "k"), case.dtype)
+    v = oracle.as_f64(logical_kv(case, b, "v"), case.dtype)
+    return oracle.attention_ref(q, k, v, [0, q1 - q0], [0, lk], case.scale, causal=True)
+
+
+def oracle_workers():
+    """Threads for oracle rows: the CPUs this process may use, at most 16 (NumPy's widening and products
+    release the interpreter lock, so sequences run side by side)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def oracle_attention(case, rows=None):
-    """float64 oracle output over logical (contiguous) K/V.  ``rows``: sequences to compute (default all)."""
-    seqs = range(case.batch) if rows is None else rows
-    outs = {}
-    for b in seqs:
-        lk = int(case.Lk[b])
-        q0, q1 = int(case.cu_seqlens_q[b]), int(case.cu_seqlens_q[b + 1])
-        q = f64(case.q[q0:q1], case.dtype)
-        if lk == 0:
-            outs[b] = np.zeros_like(q)
-            continue
-        k = oracle.as_f64(logical_kv(case, b, "k"), case.dtype)
-        v = oracle.as_f64(logical_kv(case, b, "v"), case.dtype)
-        outs[b] = oracle.attention_ref(q, k, v, [0, q1 - q0], [0, lk], case.scale, causal=True)
-    return outs
+    """float64 oracle output over logical (contiguous) K/V.  ``rows``: sequences to compute (default all),
+    each sequence an independent oracle call, run on a pool of threads."""
+    seqs = list(range(case.batch) if rows is None else rows)
+    if len(seqs) <= 2:
+        return {b: _oracle_one(case, b) for b in seqs}
+    with ThreadPoolExecutor(max_workers=oracle_workers()) as pool:
+        results = list(pool.map(lambda b: _oracle_one(case, b), seqs))
+    return dict(zip(seqs, results))
 
 
 def max_abs_err(got, want):

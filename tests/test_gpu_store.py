@@ -142,3 +142,27 @@ def test_store_zero_tokens_is_a_noop(pkv):
     pkv.kv_store(empty, empty, kc, vc, torch.empty(0, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert bool((kc == 1).all()) and bool((vc == 1).all())
+
+
+def test_binding_rejects_short_metadata(pkv):
+    """The kernels read cu_seqlens [batch + 1] and context_lens [batch]; shorter tensors are refused before any
+    launch (the C ABI cannot see their lengths)."""
+    bt = i32(np.arange(6).reshape(3, 2))
+    with pytest.raises(ValueError):
+        pkv.kv_slot_mapping(bt, 4, 8, cu_seqlens_q=i32([0, 3, 8]))            # 3 entries for batch 3
+    with pytest.raises(ValueError):
+        pkv.kv_slot_mapping(bt, 4, 8, cu_seqlens_q=i32([0, 3, 5, 8]), cu_seqlens_k=i32([0, 4]))
+    with pytest.raises(ValueError):
+        pkv.kv_slot_mapping(bt, 4, 3, context_lens=i32([1, 2]))
+    with pytest.raises(ValueError):
+        pkv.kv_slot_mapping(bt, 4, 3)                                          # neither mode
+    got = pkv.kv_slot_mapping(bt, 4, 3, context_lens=i32([1, 5, 0]))
+    assert to_host(got).tolist() == [0, 3 * 4 + 0, -1]   # row 1: position 4 is cell 0 of block bt[1][1] = 3
+
+
+def test_slot_beyond_int32_is_none(pkv):
+    """A block id whose slot does not fit an int32 gives -1 (formed in 64 bits, never wrapped into range)."""
+    big = (2 ** 31) // 256 + 5                      # big * 256 > INT32_MAX
+    bt = i32([[big], [3]])
+    got = pkv.kv_slot_mapping(bt, 256, 2, context_lens=i32([10, 10]))
+    assert to_host(got).tolist() == [-1, 3 * 256 + 9]

@@ -116,11 +116,8 @@ def test_long_decode_batch256_padded(pkv):
     np.testing.assert_array_equal(sm_h, oracle_slot_mapping(case))
     assert np.all(sm_h[224:] == -1)
     _check_store(case, kc, vc, sm_h)
-    # the oracle on a seeded sample of real rows, always including the shortest and longest context
-    rng = np.random.default_rng(55)
-    sample = sorted(set(rng.choice(real, 10, replace=False).tolist()) |
-                    {int(real[np.argmin(case.Lk[real])]), int(real[np.argmax(case.Lk[real])])})
-    _check_attention(case, out, sample)
+    # every real row against the oracle (padding rows are checked to be zero below)
+    _check_attention(case, out, real.tolist())
     assert bool((out[224:] == 0).all())  # padding rows
 
 
