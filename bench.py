@@ -15,7 +15,9 @@ The same JSON line carries:
                 make the GPU drain before each one), against MI355X's 8 TB/s HBM peak; ``traffic`` from
                 rocprofv3 counters kept in profiles/ (null if the kernel source changed since they were
                 taken);
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload, BLAS pinned to one thread;
+  cpu_baseline  the CPU oracle on the host's cores (a pool of worker processes, one BLAS thread each, run
+                before the GPU is touched): decode attention of the whole batch-64 decode workload, with the
+                varlen prefill (TFLOP/s) and the store sweep (GB/s) beside it;
   secondary     the unfused decode step and call, varlen prefill TFLOP/s (8 sequences of 128-2048), prefix-cache
                 prefill TFLOP/s (16 sequences), the store sweep GB/s (N=16384), the long padded decode GB/s
                 (batch 256) and the fused QK-Norm + RoPE + store GB/s (the 8 prefill sequences' tokens); the
@@ -230,9 +232,33 @@ def bench_store(pkv, torch, steps, warmup):
     n = len(sw.slots[0])
     row = sw.num_kv_heads * sw.head_dim * 2
     moved = 2 * n * row * 2 + 4 * n  # read + write of K and V rows, plus the slots
-    del kc, vc
+
+    # References for the same bytes and rotation, by the framework's own kernels (not this library's): its
+    # scatter with the same slots (contiguous row reads, random distinct 2 KiB row writes), and a contiguous
+    # device copy of the same rows (the read + write pattern with no scatter at all).
+    d = sw.num_kv_heads * sw.head_dim
+    idx64 = [s.long() for s in slots]
+    kflat, vflat = kc.view(-1, d), vc.view(-1, d)
+
+    def torch_scatter(i):
+        s = i % len(slots)
+        kflat.index_copy_(0, idx64[s], sw.key[s].view(-1, d))
+        vflat.index_copy_(0, idx64[s], sw.value[s].view(-1, d))
+
+    dst_k = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+    dst_v = torch.empty_like(dst_k)
+
+    def torch_copy(i):
+        s = i % len(slots)
+        dst_k.copy_(sw.key[s].view(-1, d))
+        dst_v.copy_(sw.value[s].view(-1, d))
+
+    scatter_ms = time_kernel(torch, torch_scatter, steps)
+    copy_ms = time_kernel(torch, torch_copy, steps)
+    del kc, vc, kflat, vflat, dst_k, dst_v
     torch.cuda.empty_cache()
-    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n, "sets": len(slots)}
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n, "sets": len(slots),
+            "torch_scatter_ms": scatter_ms, "torch_copy_ms": copy_ms, "copy_bytes": 2 * n * row * 2}
 
 
 def bench_decode_latency(pkv, torch, reps):
@@ -362,41 +388,139 @@ def bench_qknorm_rope_store(pkv, torch, make, steps, warmup, layers):
 
 
 # ------------------------------------------------------------------------------------------------ CPU side
+#
+# The oracle as it stands (float64 NumPy, test infrastructure), timed on the host's cores: independent oracle
+# calls -- one per sequence (decode) or per (sequence, kv head) (prefill) -- run on a pool of worker processes
+# forked before this process touches the GPU, one BLAS thread each.  Processes, not threads: the oracle's
+# per-row loop holds the interpreter lock.
 
-def cpu_baseline(min_seconds=10.0, n_seqs=16):
-    """The oracle's decode step (slot_mapping, store, attention) on the first ``n_seqs`` sequences of
-    the batch-64 decode workload (same context lengths, shapes and distributions), repeated until ``min_seconds`` elapsed."""
+_CPU = {}  # host data the forked workers inherit
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers():
+    """The CPUs this process may run on, at most 16 (one GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def _decode_task(b):
+    """The oracle's decode of sequence b over the blocks its table names (a compact copy of them, table
+    renumbered 0..n-1: the same logical keys and values), widened to float64 as the oracle consumes them."""
+    import numpy as np
+    import oracle
+    d = _CPU["decode"]
+    n = int(-(-int(d["ctx"][b]) // 256))
+    blocks = d["bt"][b, :n]
+    kc = oracle.as_f64(d["kc"][blocks], "bf16")
+    vc = oracle.as_f64(d["vc"][blocks], "bf16")
+    table = np.arange(n, dtype=np.int32)[None]
+    return oracle.decode_ref(d["q"][b:b + 1], kc, vc, d["ctx"][b:b + 1], table, 256, d["scale"])
+
+
+def _prefill_task(bg):
+    """The oracle's causal attention of sequence b for the query heads of kv head g."""
+    import oracle
+    b, g = bg
+    p = _CPU["prefill"]
+    q0, q1 = int(p["cu"][b]), int(p["cu"][b + 1])
+    grp = p["group"]
+    return oracle.attention_ref(p["q"][q0:q1, g * grp:(g + 1) * grp], p["k"][q0:q1, g:g + 1],
+                                p["v"][q0:q1, g:g + 1], [0, q1 - q0], [0, q1 - q0], p["scale"], causal=True)
+
+
+def _time_pool(pool, fn, tasks, min_seconds):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        list(pool.map(fn, tasks, chunksize=1))
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    return reps, (time.perf_counter() - t0) / reps
+
+
+def cpu_baseline(min_seconds=8.0):
+    """The oracle on the host: decode attention of the whole batch-64 decode workload (KV GB/s), causal
+    attention of the whole 8-sequence varlen prefill workload (TFLOP/s), and the store of an eighth of the store
+    sweep (GB/s).  Must run before the GPU is initialised (the pool is forked)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
     import numpy as np
     import oracle
     import workloads
-    rng = np.random.default_rng(2)
-    ctx = rng.integers(512, 4096, size=64, endpoint=True)[:n_seqs]
-    case = workloads.decode_case(ctx, num_blocks=sum(math.ceil(int(c) / 256) for c in ctx), seed=2)
-    cache = workloads.nan_cache_host(case.num_blocks, 256, 8, 128, "bf16")
-    hist_sm = oracle.slot_mapping_ref(case.block_tables, 256, int(case.cu_hist[-1]), cu_seqlens_q=case.cu_hist,
-                                      cu_seqlens_k=case.cu_hist)
-    kc, vc = oracle.store_ref(case.hist_k, case.hist_v, cache, cache, hist_sm)
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):
-        reps, secs = _time_oracle_step(case, kc, vc, min_seconds)
-    kv_bytes = int(ctx.sum()) * 2 * 8 * 128 * 2
-    return {"value": round(kv_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the batch-64 decode workload's first {n_seqs} sequences (sum ctx {int(ctx.sum())}), full decode step "
-                      f"(slot_mapping + store + attention, float64), {reps} repetitions, {secs:.2f} s each"}
+    _one_blas_thread()
+    workers = cpu_workers()
+    # decode: the cache after the oracle's slot_mapping + store of every sequence's history and new token
+    c2 = workloads.decode_batch64(device="cpu")
+    cache = workloads.nan_cache_host(c2.num_blocks, 256, 8, 128, "bf16")
+    hist_sm = oracle.slot_mapping_ref(c2.block_tables, 256, int(c2.cu_hist[-1]), cu_seqlens_q=c2.cu_hist,
+                                      cu_seqlens_k=c2.cu_hist)
+    kc, vc = oracle.store_ref(c2.hist_k, c2.hist_v, cache, cache, hist_sm)
+    del cache
+    sm = oracle.slot_mapping_ref(c2.block_tables, 256, c2.batch, context_lens=c2.context_lens)
+    kc, vc = oracle.store_ref(c2.k, c2.v, kc, vc, sm)
+    _CPU["decode"] = {"kc": kc, "vc": vc, "bt": c2.block_tables, "ctx": c2.context_lens,
+                      "q": oracle.as_f64(c2.q, "bf16"), "scale": c2.scale}
+    # prefill: the new tokens' q, k, v widened once (the attention reads this step's rows)
+    c3 = workloads.varlen_prefill_8seq(device="cpu")
+    _CPU["prefill"] = {"q": oracle.as_f64(c3.q, "bf16"), "k": oracle.as_f64(c3.k, "bf16"),
+                       "v": oracle.as_f64(c3.v, "bf16"), "cu": c3.cu_seqlens_q, "scale": c3.scale,
+                       "group": c3.num_q_heads // c3.num_kv_heads}
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork"),
+                             initializer=_one_blas_thread) as pool:
+        list(pool.map(time.sleep, [0.05] * workers))  # every worker started before the clock runs
+        d_reps, d_secs = _time_pool(pool, _decode_task, range(c2.batch), min_seconds)
+        tasks = sorted(((b, g) for b in range(c3.batch) for g in range(c3.num_kv_heads)),
+                       key=lambda bg: -int(c3.Lq[bg[0]]))  # longest first
+        p_reps, p_secs = _time_pool(pool, _prefill_task, tasks, min_seconds / 2)
+    _CPU.clear()
+    del kc, vc
+    # store: one sequential scatter into one cache (the oracle copies the cache, then writes the rows); an
+    # eighth of the sweep -- 2048 tokens into a 512-block cache, the same tokens per cache slot
+    sw = workloads.store_sweep(2048, n_sets=1, num_blocks=512, device="cpu")
+    sc = workloads.nan_cache_host(sw.num_blocks, sw.block_size, sw.num_kv_heads, sw.head_dim, "bf16")
+    s_reps, t0 = 0, time.perf_counter()
+    while s_reps < 1 or time.perf_counter() - t0 < min_seconds / 4:
+        oracle.store_ref(sw.key[0], sw.value[0], sc, sc, sw.slots[0])
+        s_reps += 1
+    s_secs = (time.perf_counter() - t0) / s_reps
+    sw_slots = sw.slots[0]
+    del sc, sw
 
-
-def _time_oracle_step(case, kc, vc, min_seconds):
-    import oracle
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        sm = oracle.slot_mapping_ref(case.block_tables, 256, case.batch, context_lens=case.context_lens)
-        kc2, vc2 = oracle.store_ref(case.k, case.v, kc, vc, sm)
-        oracle.decode_ref(oracle.as_f64(case.q, "bf16"), oracle.as_f64(kc2, "bf16"), oracle.as_f64(vc2, "bf16"),
-                          case.context_lens, case.block_tables, 256, case.scale)
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds or reps >= 1000:
-            break
-    return reps, (time.perf_counter() - t0) / reps
+    kv_bytes = int(c2.Lk.astype(int).sum()) * 2 * 8 * 128 * 2
+    flops = 4 * c3.head_dim * c3.num_q_heads * int(sum(int(L) * (int(L) + 1) // 2 for L in c3.Lq))
+    n_store = len(sw_slots)
+    store_bytes = 2 * n_store * 1024 * 2 * 2 + 4 * n_store
+    model = cpu_model()
+    return {
+        "value": round(kv_bytes / d_secs / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+        "cpu_model": model, "cpus_visible": len(os.sched_getaffinity(0)),
+        "sample": f"decode attention of the whole batch-64 decode workload (64 sequences, sum ctx "
+                  f"{int(c2.Lk.sum())}, float64), one oracle call per sequence over {workers} worker processes "
+                  f"(one BLAS thread each), {d_reps} repetitions of {d_secs:.3f} s",
+        "prefill": {"value": round(flops / p_secs / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
+                    "sample": f"causal attention of the whole 8-sequence varlen prefill workload "
+                              f"({int(c3.Lq.sum())} tokens, {flops / 1e9:.1f} GFLOP of causal pairs, float64), "
+                              f"one oracle call per (sequence, kv head), {p_reps} repetitions of {p_secs:.3f} s"},
+        "store": {"value": round(store_bytes / s_secs / 1e9, 4), "unit": "GB/s", "cores": 1,
+                  "sample": f"an eighth of the store sweep: {n_store} tokens into a 512-block cache (the same "
+                            f"tokens per slot; the oracle copies both 256 MiB caches, then writes the rows; one "
+                            f"process), {s_reps} repetitions of {s_secs:.3f} s"},
+    }
 
 
 # ------------------------------------------------------------------------------------------------ main
@@ -418,6 +542,12 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu:
+        # before anything touches the GPU: the oracle's worker processes are forked from this one
+        log(f"cpu oracle baseline ({cpu_workers()} worker processes)")
+        cpu = cpu_baseline()
 
     import torch
     import paged_kv_cache_300_amd as pkv
@@ -479,7 +609,11 @@ def main():
             secondary["store_sweep_16k"] = {"value": round(gbs, 1), "unit": "GB/s",
                                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                                  "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
-                                                 "tokens": st["tokens"], "sets_rotated": st["sets"]}
+                                                 "tokens": st["tokens"], "sets_rotated": st["sets"],
+                                                 "reference_torch_index_copy_GBps":
+                                                     round(st["copy_bytes"] / (st["torch_scatter_ms"] * 1e-3) / 1e9, 1),
+                                                 "reference_contiguous_copy_GBps":
+                                                     round(st["copy_bytes"] / (st["torch_copy_ms"] * 1e-3) / 1e9, 1)}
         if fd is not None:
             gbk = fd["kv_bytes"] / (fd["kernel_ms"] * 1e-3) / 1e9
             secondary["decode_step_unfused_batch64"] = {
@@ -503,11 +637,6 @@ def main():
                                                  "frac_hbm_peak": round(gbs5 / HBM_PEAK_GBS, 4),
                                                  "kernel_ms": round(d5["kernel_ms"], 4), "kv_bytes": d5["kv_bytes"],
                                                  "step_ms": round(d5["wall_ms"], 4)}
-
-    cpu = None
-    if not args.no_cpu:
-        log("cpu oracle baseline")
-        cpu = cpu_baseline()
 
     line = {
         "metric": METRIC,

@@ -211,3 +211,23 @@ def test_uniform_scores_give_mean_over_any_split():
     v = _rand(rng, 10, 3)
     o, _ = oracle.online_softmax_blocks(np.full(10, 2.5), v, [3, 3, 4])
     np.testing.assert_allclose(o, v.mean(axis=0), rtol=1e-13)
+
+
+def test_generator_rounding_is_nearest_even():
+    """The seeded generator's float32 -> bf16 rounding (shared input preparation, not method arithmetic) is
+    round-to-nearest-even: it agrees with torch's CPU conversion on ties, carries into the exponent, signed
+    zeros, infinities and random patterns."""
+    import torch
+    import workloads
+    rng = np.random.default_rng(9)
+    pats = np.concatenate([
+        rng.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32),
+        np.array([0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0x3FFF8000, 0x7F7F8000, 0x7F7FFFFF,
+                  0x80000000, 0x00000000, 0x7F800000, 0xFF800000, 0x00008000, 0x80018000], dtype=np.uint32)])
+    x = pats.view(np.float32)
+    finite = np.isfinite(x)
+    got = workloads.f32_to_bf16_bits(x[finite])
+    want = torch.from_numpy(x[finite].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    inf = workloads.f32_to_bf16_bits(np.array([np.inf, -np.inf], np.float32))
+    assert inf.tolist() == [0x7F80, 0xFF80]

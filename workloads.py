@@ -46,8 +46,10 @@ WORKLOADS = {
 
 def f32_to_bf16_bits(x):
     """Round float32 values to bf16 (nearest, ties to even); returns the raw 16-bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # 32-bit sums: only patterns >= 0xFFFF8000 (negative NaNs) wrap, and they give 0 either way, as the
+    # 17-bit quotient 0x10000 of an exact sum would after the cast to 16 bits
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 
