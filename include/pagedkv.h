@@ -214,6 +214,28 @@ int attn_decode_paged_store(const void* q, int64_t q_stride, const void* k_new, 
                             int32_t* slot_mapping_out, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
                             hipStream_t stream);
 
+/*
+ * attn_decode_paged_store_noalloc -- attn_decode_paged_store for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument; the workspace lives in a static device array of 32 MiB inside the library (one per GPU, held
+ * from the first call on that GPU until the process ends).  Nothing is allocated: no hipMalloc, no hipFree.
+ *
+ * Arguments, results (bit for bit) and errors: as attn_decode_paged_store without workspace /
+ * workspace_bytes.  The caller still provides every input and output.  A call whose workspace
+ * (attn_decode_workspace_bytes) exceeds 32 MiB returns PKV_ERR_WORKSPACE before anything is enqueued (batch
+ * 64 with 16 query heads needs about 9 MiB; up to about 3000 rows of 16 query heads fit).  Every call on one GPU
+ * shares its array, whose contents after a call are left as they are: calls that may overlap on one GPU
+ * (different streams without ordering between them, several host threads) race on it and must be
+ * serialised by the caller; calls on one stream are ordered and safe.
+ */
+int attn_decode_paged_store_noalloc(const void* q, int64_t q_stride, const void* k_new, int64_t k_new_stride,
+                                    const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache,
+                                    int32_t num_blocks, const int32_t* context_lens, const int32_t* block_tables,
+                                    int32_t batch, int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    float softmax_scale, void* out, int32_t* slot_mapping_out, pkv_dtype dtype,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

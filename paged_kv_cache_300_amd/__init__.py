@@ -26,6 +26,7 @@ from ._lib import (
     attn_decode_workspace_bytes,
     attn_decode_paged,
     attn_decode_paged_store,
+    attn_decode_paged_store_noalloc,
 )
 from .sublayer import AttentionSublayer
 
@@ -43,5 +44,6 @@ __all__ = [
     "attn_decode_workspace_bytes",
     "attn_decode_paged",
     "attn_decode_paged_store",
+    "attn_decode_paged_store_noalloc",
     "AttentionSublayer",
 ]

@@ -58,6 +58,9 @@ def lib():
     L.attn_decode_paged_store.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                           i32, f32, vp, vp, vp, sz, ctypes.c_int, vp]
     L.attn_decode_paged_store.restype = ctypes.c_int
+    L.attn_decode_paged_store_noalloc.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, vp, vp, i32, i32, i32,
+                                                  i32, i32, i32, f32, vp, vp, ctypes.c_int, vp]
+    L.attn_decode_paged_store_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -313,11 +316,8 @@ def attn_decode_paged(q, k_cache, v_cache, cache_seqlens, block_table, softmax_s
     return out
 
 
-def attn_decode_paged_store(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, softmax_scale, out=None,
-                            workspace=None, slot_mapping_out=None):
-    """The decode step in one call: each row's new k/v ([B, Hkv, hd]) to its slot (position cache_seqlens[b] - 1
-    through block_table), then attention over the cache including it; returns [B, Hq, hd].  Same results as
-    kv_slot_mapping + kv_store + attn_decode_paged.  ``slot_mapping_out`` ([B] int32) receives the slots."""
+def _decode_store_args(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, out, slot_mapping_out):
+    """Shape/dtype checks of the fused decode step; returns (q as [B, Hq, hd], its stride, k/v strides, out)."""
     _dev(q, "q")
     if q.dim() == 4 and q.shape[1] == 1:
         q = q[:, 0]
@@ -341,18 +341,48 @@ def attn_decode_paged_store(q, k_new, v_new, k_cache, v_cache, cache_seqlens, bl
         _meta(slot_mapping_out, "slot_mapping_out")
         if slot_mapping_out.numel() != b:
             raise ValueError("slot_mapping_out must have one entry per row")
-    max_blocks = block_table.shape[1]
-    need = attn_decode_workspace_bytes(b, hq, hkv, hd, max_blocks, bs, q.dtype)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((b, hq, hd), dtype=q.dtype, device=q.device)
     elif out.shape != (b, hq, hd) or not out.is_contiguous() or out.dtype != q.dtype:
         raise ValueError("out must be a contiguous [B, Hq, head_dim] tensor of q's dtype")
+    return q, qs, ks, vs, out
+
+
+def attn_decode_paged_store(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, softmax_scale, out=None,
+                            workspace=None, slot_mapping_out=None):
+    """The decode step in one call: each row's new k/v ([B, Hkv, hd]) to its slot (position cache_seqlens[b] - 1
+    through block_table), then attention over the cache including it; returns [B, Hq, hd].  Same results as
+    kv_slot_mapping + kv_store + attn_decode_paged.  ``slot_mapping_out`` ([B] int32) receives the slots."""
+    q, qs, ks, vs, out = _decode_store_args(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, out,
+                                            slot_mapping_out)
+    b, hq, hd = q.shape
+    num_blocks, bs, hkv, _ = k_cache.shape
+    max_blocks = block_table.shape[1]
+    need = attn_decode_workspace_bytes(b, hq, hkv, hd, max_blocks, bs, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().attn_decode_paged_store(_ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(k_cache), _ptr(v_cache),
                                        num_blocks, _ptr(cache_seqlens), _ptr(block_table), b, max_blocks, bs, hq, hkv,
                                        hd, float(softmax_scale), _ptr(out), _ptr(slot_mapping_out), _ptr(workspace),
                                        ws_bytes, _dtype_code(q), _stream(q))
     _check("attn_decode_paged_store", rc)
+    return out
+
+
+def attn_decode_paged_store_noalloc(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, softmax_scale,
+                                    out, slot_mapping_out=None):
+    """attn_decode_paged_store whose workspace is the library's static scratch (no workspace argument, and
+    nothing allocated here either: ``out`` is required).  Calls that overlap on one GPU race on the scratch."""
+    if out is None:
+        raise ValueError("out is required (this call allocates nothing)")
+    q, qs, ks, vs, out = _decode_store_args(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, out,
+                                            slot_mapping_out)
+    b, hq, hd = q.shape
+    num_blocks, bs, hkv, _ = k_cache.shape
+    rc = lib().attn_decode_paged_store_noalloc(_ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(k_cache),
+                                               _ptr(v_cache), num_blocks, _ptr(cache_seqlens), _ptr(block_table), b,
+                                               block_table.shape[1], bs, hq, hkv, hd, float(softmax_scale), _ptr(out),
+                                               _ptr(slot_mapping_out), _dtype_code(q), _stream(q))
+    _check("attn_decode_paged_store_noalloc", rc)
     return out

@@ -294,4 +294,34 @@ int attn_decode_paged_store(const void* q, int64_t q_stride, const void* k_new, 
                      softmax_scale, out, workspace, workspace_bytes, dtype, stream, &f);
 }
 
+int attn_decode_paged_store_noalloc(const void* q, int64_t q_stride, const void* k_new, int64_t k_new_stride,
+                                    const void* v_new, int64_t v_new_stride, void* k_cache, void* v_cache,
+                                    int32_t num_blocks, const int32_t* context_lens, const int32_t* block_tables,
+                                    int32_t batch, int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    float softmax_scale, void* out, int32_t* slot_mapping_out, pkv_dtype dtype,
+                                    hipStream_t stream) {
+  g_error.clear();
+  // The workspace attn_decode_paged_store would need, taken from the static scratch: refused when larger.
+  const size_t need = attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                                  block_size, dtype);
+  if (need > pkv::kDecodeScratchBytes)
+    return fail(PKV_ERR_WORKSPACE,
+                "attn_decode_paged_store_noalloc: %zu bytes of workspace needed (batch %d, %d query heads), the "
+                "static scratch holds %zu",
+                need, batch, num_q_heads, pkv::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0 && batch > 0) {
+    const hipError_t e = pkv::decode_static_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "attn_decode_paged_store_noalloc scratch lookup");
+  }
+  pkv::DecodeStoreArgs f;
+  f.k_new = k_new; f.k_new_stride = k_new_stride; f.v_new = v_new; f.v_new_stride = v_new_stride;
+  f.slot_out = slot_mapping_out;
+  return decode_call("attn_decode_paged_store_noalloc launch", q, q_stride, k_cache, v_cache, num_blocks,
+                     context_lens, block_tables, batch, max_blocks_per_seq, block_size, num_q_heads, num_kv_heads,
+                     head_dim, softmax_scale, out, scratch, scratch ? pkv::kDecodeScratchBytes : 0, dtype, stream,
+                     &f);
+}
+
 }  // extern "C"

@@ -550,6 +550,29 @@ hipError_t launch_g(DecodeKernelArgs& p, hipStream_t stream) {
 
 }  // namespace
 
+// Scratch for callers that cannot allocate (attn_decode_paged_store_noalloc): the decode workspace in a
+// file-scope device array, one copy per GPU, held until the process ends.  Host code never uses the array's
+// name as an address (on the host it is only a stand-in); its device address is looked up once per device,
+// with that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_static_scratch(void** ptr) {
+  static std::atomic<void*> per_device[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = per_device[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 bool decode_fast_supported(int head_dim, int group, bool bf16) {
   return bf16 && head_dim == HD && (group == 1 || group == 2 || group == 4);
 }

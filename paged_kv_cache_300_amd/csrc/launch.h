@@ -60,6 +60,10 @@ struct DecodeStoreArgs {
 // fused == NULL: decode over the cache as it is; else the new token of each row is stored and attended too.
 hipError_t launch_decode_bf16(const AttnArgs& a, const DecodePlan& plan, void* workspace, hipStream_t stream,
                               const DecodeStoreArgs* fused = nullptr);
+// The decode workspace of attn_decode_paged_store_noalloc: a static device array of kDecodeScratchBytes, its
+// address on the current device (looked up on the first call on each device).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_static_scratch(void** ptr);
 // Any dtype and shape: the new token of each decode row to its slot (context_lens[b] - 1 through the block
 // table), optionally writing slot_mapping; rows with no slot write nothing.
 hipError_t launch_decode_store(const DecodeStoreArgs& s, const int32_t* context_lens, const int32_t* block_tables,

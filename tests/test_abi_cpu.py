@@ -184,3 +184,16 @@ def test_c_program_uses_the_abi(tmp_path):
     assert res.returncode == 0, res.stderr[-2000:]
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0 and run.stdout.strip() == "ok", run.stdout + run.stderr
+
+
+def test_noalloc_decode_refuses_oversized_workspace_on_host():
+    """The allocation-free fused decode takes its workspace from a fixed 32 MiB static array: a batch whose
+    workspace would not fit is refused with the workspace code before any device call."""
+    pkv, L = _lib()
+    fake = ctypes.c_void_p(0x1000)  # 16-byte aligned, never dereferenced: the size check comes first
+    need = L.attn_decode_workspace_bytes(20000, 16, 8, 128, 16, 256, pkv.PKV_BF16)
+    assert need > 32 << 20
+    rc = L.attn_decode_paged_store_noalloc(fake, 2048, fake, 1024, fake, 1024, fake, fake, 4096, fake, fake, 20000,
+                                           16, 256, 16, 8, 128, ctypes.c_float(0.088), fake, None, pkv.PKV_BF16, None)
+    assert rc == -3
+    assert "static scratch" in _err(L)
