@@ -50,7 +50,14 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  /* Range markers, not dtypes: they give the type every int32 value, so whatever a C caller passes is a
+   * value of the type (and is refused with PKV_ERR_INVALID_ARG unless it names a dtype above). */
+  PKV_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  PKV_DTYPE_RANGE_MAX_ = 2147483647
+} pkv_dtype;
 
 enum {
   PKV_OK = 0,
@@ -163,8 +170,9 @@ size_t attn_prefill_workspace_bytes(int32_t batch, int32_t num_q_tokens, int32_t
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_paged needs for these sizes
- * (0 if none).  The split of long contexts into independently reduced pieces depends only on these
- * arguments, so the same workspace serves every call with the same sizes.
+ * (0 if none, and 0 for sizes the call refuses: batch or num_q_heads above 65535, contexts beyond 2^31
+ * tokens, invalid head counts or dtype).  The split of long contexts into independently reduced pieces
+ * depends only on these arguments, so the same workspace serves every call with the same sizes.
  */
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype dtype);
@@ -221,8 +229,9 @@ int attn_decode_paged_store(const void* q, int64_t q_stride, const void* k_new, 
  * from the first call on that GPU until the process ends).  Nothing is allocated: no hipMalloc, no hipFree.
  *
  * Arguments, results (bit for bit) and errors: as attn_decode_paged_store without workspace /
- * workspace_bytes.  The caller still provides every input and output.  A call whose workspace
- * (attn_decode_workspace_bytes) exceeds 32 MiB returns PKV_ERR_WORKSPACE before anything is enqueued (batch
+ * workspace_bytes.  The caller still provides every input and output.  Arguments are checked first, as in
+ * attn_decode_paged_store; then a call whose workspace (attn_decode_workspace_bytes) exceeds 32 MiB returns
+ * PKV_ERR_WORKSPACE before anything is enqueued (batch
  * 64 with 16 query heads needs about 9 MiB; up to about 3000 rows of 16 query heads fit).  Every call on one GPU
  * shares its array, whose contents after a call are left as they are: calls that may overlap on one GPU
  * (different streams without ordering between them, several host threads) race on it and must be

@@ -47,11 +47,12 @@ int check_heads(int32_t hq, int32_t hkv, int32_t hd) {
 
 // attn_decode_paged and attn_decode_paged_store share their checks and dispatch; fused != NULL also stores each
 // row's new token (fast path: inside the decode kernel; other shapes: a store kernel, then the decode).
+// static_ws: the workspace is the library's static scratch (looked up only once every check has passed).
 int decode_call(const char* name, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                 int32_t num_blocks, const int32_t* context_lens, const int32_t* block_tables, int32_t batch,
                 int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
                 int32_t head_dim, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                pkv_dtype dtype, hipStream_t stream, const pkv::DecodeStoreArgs* fused) {
+                pkv_dtype dtype, hipStream_t stream, const pkv::DecodeStoreArgs* fused, bool static_ws = false) {
   if (!valid_dtype(dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
   if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
   if (batch < 0 || num_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "batch and num_blocks must be >= 0");
@@ -91,6 +92,14 @@ int decode_call(const char* name, const void* q, int64_t q_stride, const void* k
   if (fast) {
     const pkv::DecodePlan plan =
         pkv::decode_plan(batch, num_q_heads, num_kv_heads, max_blocks_per_seq * block_size);
+    if (static_ws) {
+      if (plan.workspace_bytes > pkv::kDecodeScratchBytes)
+        return fail(PKV_ERR_WORKSPACE, "%s: %zu bytes of workspace needed (batch %d, %d query heads), the static "
+                    "scratch holds %zu", name, plan.workspace_bytes, batch, num_q_heads, pkv::kDecodeScratchBytes);
+      if (const hipError_t e = pkv::decode_static_scratch(&workspace); e != hipSuccess)
+        return hip_status(e, name);
+      workspace_bytes = pkv::kDecodeScratchBytes;
+    }
     if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
       return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace_bytes,
                   workspace ? workspace_bytes : size_t(0));
@@ -258,8 +267,9 @@ size_t attn_prefill_workspace_bytes(int32_t batch, int32_t num_q_tokens, int32_t
 
 size_t attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype dtype) {
-  if (batch <= 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads || max_blocks_per_seq < 1 ||
-      block_size < 1 || !valid_dtype(dtype))
+  // Sizes the calls refuse (batch or query heads beyond a grid dimension) need no workspace either.
+  if (batch <= 0 || batch > kMaxGridYZ || num_q_heads < 1 || num_q_heads > kMaxGridYZ || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads || max_blocks_per_seq < 1 || block_size < 1 || !valid_dtype(dtype))
     return 0;
   if (!pkv::decode_fast_supported(head_dim, num_q_heads / num_kv_heads, dtype == PKV_BF16)) return 0;
   const int64_t max_ctx = int64_t(max_blocks_per_seq) * block_size;
@@ -302,26 +312,12 @@ int attn_decode_paged_store_noalloc(const void* q, int64_t q_stride, const void*
                                     float softmax_scale, void* out, int32_t* slot_mapping_out, pkv_dtype dtype,
                                     hipStream_t stream) {
   g_error.clear();
-  // The workspace attn_decode_paged_store would need, taken from the static scratch: refused when larger.
-  const size_t need = attn_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                                                  block_size, dtype);
-  if (need > pkv::kDecodeScratchBytes)
-    return fail(PKV_ERR_WORKSPACE,
-                "attn_decode_paged_store_noalloc: %zu bytes of workspace needed (batch %d, %d query heads), the "
-                "static scratch holds %zu",
-                need, batch, num_q_heads, pkv::kDecodeScratchBytes);
-  void* scratch = nullptr;
-  if (need > 0 && batch > 0) {
-    const hipError_t e = pkv::decode_static_scratch(&scratch);
-    if (e != hipSuccess) return hip_status(e, "attn_decode_paged_store_noalloc scratch lookup");
-  }
   pkv::DecodeStoreArgs f;
   f.k_new = k_new; f.k_new_stride = k_new_stride; f.v_new = v_new; f.v_new_stride = v_new_stride;
   f.slot_out = slot_mapping_out;
-  return decode_call("attn_decode_paged_store_noalloc launch", q, q_stride, k_cache, v_cache, num_blocks,
-                     context_lens, block_tables, batch, max_blocks_per_seq, block_size, num_q_heads, num_kv_heads,
-                     head_dim, softmax_scale, out, scratch, scratch ? pkv::kDecodeScratchBytes : 0, dtype, stream,
-                     &f);
+  return decode_call("attn_decode_paged_store_noalloc", q, q_stride, k_cache, v_cache, num_blocks, context_lens,
+                     block_tables, batch, max_blocks_per_seq, block_size, num_q_heads, num_kv_heads, head_dim,
+                     softmax_scale, out, nullptr, 0, dtype, stream, &f, /*static_ws=*/true);
 }
 
 }  // extern "C"

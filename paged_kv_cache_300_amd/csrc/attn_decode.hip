@@ -492,7 +492,7 @@ Layout workspace_layout(int batch, int num_q_heads) {
   Layout L;
   const size_t slots = size_t(MAX_WORKERS) + size_t(batch);
   L.cu = 0;
-  L.acc = align256(size_t(batch + 1) * sizeof(int64_t));
+  L.acc = align256((size_t(batch) + 1) * sizeof(int64_t));
   L.ml = L.acc + align256(slots * num_q_heads * HD * sizeof(float));
   L.total = L.ml + align256(slots * num_q_heads * 2 * sizeof(float));
   return L;
