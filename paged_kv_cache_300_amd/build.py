@@ -18,7 +18,10 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["abi.cpp", "slot_store.hip", "qknorm_rope_store.hip", "attn_generic.hip", "attn_decode.hip",
-           "attn_prefill.hip"]
+           "attn_prefill.hip", "attn_prefill_w32.hip"]
+# Per-source flags.  The 32x32 prefill keeps MFMA results in VGPRs (its exponentials read the scores directly);
+# the query operand and the rest of its 512 registers go to AGPRs.
+EXTRA_FLAGS = {"attn_prefill_w32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -44,7 +47,7 @@ def _hipcc():
 
 def _compile(hipcc, src):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
