@@ -23,6 +23,8 @@
 //    more block of V^T whose first row is ones, which takes its sum off the vector units.
 //  * Only tiles that cross the causal diagonal or the end of the keys are masked.  Work-groups are
 //    launched heaviest query tile first so the long causal rows do not form the tail.
+//  * GQA groups of 2 with contiguous rows or a paged cache of power-of-two blocks >= 64 and a positive scale go to
+//    the 32x32 kernel of attn_prefill_w32.hip instead (same units, same planner); these kernels serve the rest.
 #include <math.h>
 
 #include <algorithm>

@@ -76,8 +76,6 @@ struct WSrc {
   const uint16_t* khead;  // kv head at row / slot 0
   const uint16_t* vhead;
   const int32_t* bt_row;  // paged: the sequence's block-table row
-  int Lk;
-  int64_t k_start;        // contiguous: first key row of the sequence
   int64_t kstride, vstride;  // elements between rows (contiguous) or slots (paged)
 };
 
@@ -93,27 +91,21 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, 
                : "m0");
 }
 
-// This wave's 16 rows (16 w .. +16) of K or V tile kt into `tile`, as 4 direct-to-LDS loads of 4 rows each.
+// A K/V tile's place in memory, uniform over the work-group: its first row (contiguous rows) or slot (paged
+// cache), and how many of its 64 rows are valid keys.  Computed once per tile: the K loads of a tile and, one
+// step later, its V loads use the same one.
+struct TileRef {
+  int64_t row;
+  int rows;
+};
+
+// This wave's 16 rows (16 w .. +16) of a K or V tile into `tile`, as 4 direct-to-LDS loads of 4 rows each.
 // Lane i of a load lands at row 16 w + 4 k + i / 16, chunk slot i % 16, so it fetches chunk (i % 16) ^ swz(row);
 // off[k] is that byte offset from the tile's first row.  The whole offset is the lane's (vector) offset, which the
 // buffer's bounds check covers: rows past `rows` read as zeros and touch no memory.
-// PAGED: `blk` is the cache block holding the tile (uniform, already checked).
-template <int MODE, bool IS_V>
-__device__ __forceinline__ void dma_rows(const PrefillKernelArgs& p, const WSrc& s, int kt, int blk, lds_u16* tile,
-                                         int w, const uint32_t (&off)[4]) {
-  const int64_t stride = IS_V ? s.vstride : s.kstride;
-  const uint16_t* head = IS_V ? s.vhead : s.khead;
-  int rows = min(s.Lk - kt * BN, BN);
-  const uint16_t* base;
-  if constexpr (MODE == LOAD_PAGED) {
-    base = head + (int64_t(blk) * p.bs + ((kt * BN) & (p.bs - 1))) * stride;
-  } else {
-    const int64_t row0 = s.k_start + int64_t(kt) * BN;
-    rows = row0 < 0 ? 0 : int(min(int64_t(rows), p.num_k_rows - row0));
-    base = head + row0 * stride;
-  }
-  rows = __builtin_amdgcn_readfirstlane(max(rows, 0));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, uint32_t(rows) * uint32_t(stride) * 2u);
+__device__ __forceinline__ void dma_rows(const uint16_t* head, int64_t stride, TileRef ref, lds_u16* tile, int w,
+                                         const uint32_t (&off)[4]) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + ref.row * stride, uint32_t(ref.rows) * uint32_t(stride) * 2u);
 #pragma unroll
   for (int k = 0; k < 4; ++k) dma16(rs, off[k], 0u, tile + (w * 16 + k * 4) * WROW);
 }
@@ -259,8 +251,6 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
     src.khead = p.k + int64_t(kvh) * HD;
     src.vhead = p.v + int64_t(kvh) * HD;
     src.bt_row = p.bt ? p.bt + int64_t(b) * p.max_blocks : nullptr;
-    src.Lk = Lk;
-    src.k_start = g.k_start;
     src.kstride = p.bt ? int64_t(p.num_kv_heads) * HD : p.k_stride;
     src.vstride = p.bt ? int64_t(p.num_kv_heads) * HD : p.v_stride;
     uint32_t koff[4], voff[4];
@@ -330,25 +320,35 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
     // Pins the weights above the mask branch that follows (otherwise they would be moved next to their products).
     auto keep = [](const u32x4 (&pb)[2]) { asm volatile("" ::"v"(pb[0]), "v"(pb[1])); };
 
-    // PAGED: block-table entries of the tiles whose loads the next step issues (V of tile kt + 1: fv, K of tile
-    // kt + 2: fk), fetched a step ahead.
+    // Tile references.  Contiguous: the sequence's rows k_start .. k_start + valid - 1 (valid also bounded by the
+    // k/v arrays).  Paged: tile kt lies in the cache block of its first key; the block-table entry of the tile
+    // whose K loads the next step issues is fetched a step ahead (fk).
+    const int valid = MODE == LOAD_PAGED ? Lk
+                                         : (g.k_start < 0 ? 0 : int(min(int64_t(Lk), p.num_k_rows - g.k_start)));
+    auto tile_ref = [&](int kt, int blk) {
+      TileRef r;
+      r.rows = __builtin_amdgcn_readfirstlane(min(max(valid - kt * BN, 0), BN));
+      r.row = MODE == LOAD_PAGED ? int64_t(blk) * p.bs + ((kt * BN) & (p.bs - 1)) : g.k_start + int64_t(kt) * BN;
+      return r;
+    };
     const __amdgpu_buffer_rsrc_t bt_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t*>(MODE == LOAD_PAGED ? src.bt_row : p.cu_k), 0, MODE == LOAD_PAGED ? p.max_blocks * 4 : 0,
         kBufferFlags);
-    int fv = 0, fk = 0, b0 = 0, b1 = 0;
+    int fk = 0, b0 = 0, b1 = 0;
     if constexpr (MODE == LOAD_PAGED) {
       b0 = bt_fetch(p, bt_rs, 0);
       b1 = bt_fetch(p, bt_rs, 1);
       fk = bt_fetch(p, bt_rs, 2);
-      fv = b1;
       b0 = bt_block(p, b0);
       b1 = bt_block(p, b1);
     }
+    const TileRef r0 = tile_ref(0, b0);
+    TileRef r1 = tile_ref(1, b1);  // the tile whose V loads the next step issues
 
     // Prologue: K and V of the first tile and K of the second; scores and maximum of the first block.
-    dma_rows<MODE, false>(p, src, 0, b0, kbuf(0), wave, koff);
-    dma_rows<MODE, true>(p, src, 0, b0, vbuf(0), wave, voff);
-    if (nt > 1) dma_rows<MODE, false>(p, src, 1, b1, kbuf(1), wave, koff);
+    dma_rows(src.khead, src.kstride, r0, kbuf(0), wave, koff);
+    dma_rows(src.vhead, src.vstride, r0, vbuf(0), wave, voff);
+    if (nt > 1) dma_rows(src.khead, src.kstride, r1, kbuf(1), wave, koff);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16_t sa, sb;  // scores of the tile's first block (sa) and second block (sb)
@@ -364,13 +364,11 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
       constexpr bool LAST = decltype(last_tag)::value;
       settle();
       if (!LAST) {
-        const int bk = MODE == LOAD_PAGED ? bt_block(p, fk) : 0, bv = MODE == LOAD_PAGED ? bt_block(p, fv) : 0;
-        if (kt + 2 < nt) dma_rows<MODE, false>(p, src, kt + 2, bk, kbuf((kt + 2) % 3), wave, koff);
-        dma_rows<MODE, true>(p, src, kt + 1, bv, vbuf((kt + 1) & 1), wave, voff);
-        if constexpr (MODE == LOAD_PAGED) {
-          fv = fk;
-          fk = bt_fetch(p, bt_rs, kt + 3);
-        }
+        const TileRef r2 = tile_ref(kt + 2, MODE == LOAD_PAGED ? bt_block(p, fk) : 0);
+        if (kt + 2 < nt) dma_rows(src.khead, src.kstride, r2, kbuf((kt + 2) % 3), wave, koff);
+        dma_rows(src.vhead, src.vstride, r1, vbuf((kt + 1) & 1), wave, voff);
+        r1 = r2;
+        if constexpr (MODE == LOAD_PAGED) fk = bt_fetch(p, bt_rs, kt + 3);
       }
       const lds_u16* vt = vbuf(kt & 1);
       u32x4 pb0[2];

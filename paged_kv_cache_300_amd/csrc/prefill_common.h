@@ -1,6 +1,6 @@
-// Shared by the prefill kernels (attn_prefill.hip: 16x16 tiles at two waves per SIMD; attn_prefill_w32.hip:
-// 32x32 tiles at one wave per SIMD): kernel arguments, per-sequence geometry, buffer-resource tile reads and the
-// longest-first planner's output.  Device helpers only; everything is inline.
+// Shared by the prefill kernels (attn_prefill.hip: 16x16 tiles, 16 tokens per wave; attn_prefill_w32.hip: 32x32
+// tiles, 32 query rows per wave; both at two waves per SIMD): kernel arguments, per-sequence geometry,
+// buffer-resource tile reads and the longest-first planner's output.  Device helpers only; everything is inline.
 #pragma once
 
 #include <math.h>
@@ -145,8 +145,9 @@ struct PlanList {
 }  // namespace pf
 
 // 32x32 MFMA prefill for GQA groups of 2 with contiguous rows or a paged cache whose block size is a power of two
-// >= 64, and a positive softmax scale (attn_prefill_w32.hip).  plan.list == NULL: one work-group per (kv head, sequence, query tile), latest
-// tiles first; else one per listed unit and kv head (grid_units units).
+// >= 64, and a positive softmax scale (attn_prefill_w32.hip).  plan.list == NULL: one work-group per (kv head,
+// sequence, query tile), sequences in chunks with each chunk's latest tiles first; else one per listed unit and kv
+// head (grid_units units).
 bool prefill_w32_supported(int group, int mode, float scale);
 hipError_t launch_prefill_w32(const pf::PrefillKernelArgs& p, int batch, int mode, pf::PlanList plan, int grid_units,
                               hipStream_t stream);
