@@ -276,6 +276,7 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
     // Scores of block kb of `ktile` into sn, interleaved with the weights of the scores in sc: eight steps of one
     // K fragment (one product) and two exponentials, K fragments read two steps ahead.
     auto qk_weights = [&](f32x16_t& sn, const lds_u16* ktile, int kb, const f32x16_t& sc, u32x4 (&pb)[2]) {
+      __builtin_amdgcn_s_setprio(1);
       const uint32_t ka = kaddr(ktile, kb, j, half);
       u32x4 kf[3];
       kf[0] = kfrag_at(ka, 0);
@@ -287,6 +288,7 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
         weight(sc, 2 * i, pb);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     // O += P V over block kb of a V tile.
     auto pv = [&](const lds_u16* vtile, int kb, const u32x4 (&pb)[2]) {
