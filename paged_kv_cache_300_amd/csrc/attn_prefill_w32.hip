@@ -298,25 +298,18 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] = mfma32(vfrag_at(va, 2 * kb + u, db), pb[u], o[db]);
     };
-    // A block's maxima: the reference maximum moves only when it is exceeded by more than 2^8; then l is rescaled
-    // at once and O just before its next P V products (settle).
-    float alpha = 1.f;
-    bool owed = false;
+    // A block's maxima: the reference maximum moves only when it is exceeded by more than 2^8 (a uniform branch,
+    // rarely taken); then l and O are rescaled at once (O after the block's P V products, which it waits for).
     auto decide = [&](const f32x16_t& s) {
       const float mx = max_blk(s, c);
-      const bool any = __any(mx > m + kRescaleSlack);  // uniform: selects, not a branch
-      const float mn = any ? fmaxf(m, mx) : m;
-      alpha = any ? fast_exp2(m - mn) : alpha;
-      l *= any ? alpha : 1.f;
-      m = mn;
-      owed = owed || any;
-    };
-    auto settle = [&]() {
-      if (owed) {
-        asm volatile("");  // keeps the branch: the rescale of O runs only when the maximum moved
+      if (__any(mx > m + kRescaleSlack)) {
+        asm volatile("");  // keeps the branch
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mn);
+        l *= alpha;
+        m = mn;
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] *= alpha;
-        owed = false;
       }
     };
     // Pins the weights above the mask branch that follows (otherwise they would be moved next to their products).
@@ -364,7 +357,6 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
     // block's maximum is reduced.  `masked`: tile kt + 1 (and so possibly kt) needs the mask.
     auto step = [&](bool masked, auto last_tag, int kt) {
       constexpr bool LAST = decltype(last_tag)::value;
-      settle();
       if (!LAST) {
         const TileRef r2 = tile_ref(kt + 2, MODE == LOAD_PAGED ? bt_block(p, fk) : 0);
         if (kt + 2 < nt) dma_rows(src.khead, src.kstride, r2, kbuf((kt + 2) % 3), wave, koff);
@@ -382,7 +374,6 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
       }
       pv(vt, 0, pb0);
       decide(sb);
-      settle();
       u32x4 pb1[2];
       if constexpr (!LAST) {
         qk_weights(sa, kbuf((kt + 1) % 3), 0, sb, pb1);
