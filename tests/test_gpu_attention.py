@@ -307,3 +307,35 @@ def test_zero_query_gives_prefix_means(pkv):
     got = oracle.as_f64(to_host(out), "bf16")
     for h in range(16):
         assert np.max(np.abs(got[:, h] - means[:, h // 2])) <= BF16_TOL
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("scale", [-0.0883883, 1e-30, 0.0883883])
+def test_prefill_scale_signs(pkv, paged, scale):
+    """GQA groups of 2 with a negative scale (served by the 16x16 kernels), a tiny positive one (every weight 1 to
+    within rounding; the 32x32 kernel) and the usual 1/sqrt(128), against the oracle [P2 §5.3 softmax_scale]."""
+    case = workloads.make_case([130, 70], [400, 70] if paged else [130, 70], num_q_heads=16, num_kv_heads=8,
+                               head_dim=128, block_size=256, num_blocks=6, dtype="bf16", seed=61, scale=scale)
+    log(f"prefill scale={scale} paged={paged}")
+    out, *_ = _run_step(pkv, case, paged)
+    _check_attention(case, out)
+
+
+def test_prefill_paged_block_size_1024(pkv):
+    """Paged prefill with 1024-token blocks: sixteen 64-key tiles per block, prefixes ending mid-block."""
+    case = workloads.make_case([300, 70, 5], [1800, 2270, 1029], num_q_heads=16, num_kv_heads=8, head_dim=128,
+                               block_size=1024, num_blocks=9, dtype="bf16", seed=62)
+    log("prefill bs=1024 lq=[300, 70, 5] prefix=[1500, 2200, 1024]")
+    out, *_ = _run_step(pkv, case, paged=True)
+    _check_attention(case, out)
+
+
+def test_prefill_grid_order_several_chunks(pkv):
+    """Causal self-attention launched in grid order (no planner) over nine sequences: two full chunks of four
+    sequences and a last chunk of one, with empty, single-token and multi-tile sequences."""
+    lq = [700, 64, 0, 513, 1, 130, 260, 65, 390]
+    case = workloads.make_case(lq, lq, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256, num_blocks=16,
+                               dtype="bf16", seed=63)
+    log(f"prefill grid order lq={lq}")
+    out, *_ = _run_step(pkv, case, paged=False, order=False)
+    _check_attention(case, out)
