@@ -261,6 +261,9 @@ def bench_store(pkv, torch, steps, warmup):
             "torch_scatter_ms": scatter_ms, "torch_copy_ms": copy_ms, "copy_bytes": 2 * n * row * 2}
 
 
+LAYERS_PER_GRAPH = 8
+
+
 def bench_decode_latency(pkv, torch, reps):
     """The decode step (attn_decode_paged_store) at fixed batch sizes, the batch padded up to each with rows of
     context 0 (slot -1), launched eagerly and replayed from a HIP graph captured once per size: time per step
@@ -304,10 +307,19 @@ def bench_decode_latency(pkv, torch, reps):
         torch.cuda.synchronize()
         graph = run_steps(torch, lambda i: g.replay(), reps, 5) * 1e3
         graph_one = single(g.replay)
+        # A model step holds one such call per layer: the same step captured LAYERS_PER_GRAPH times in one graph
+        # (as a serving loop captures a whole forward pass), replayed back to back, time per decode step.
+        g8 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g8):
+            for _ in range(LAYERS_PER_GRAPH):
+                step()
+        torch.cuda.synchronize()
+        graph8 = run_steps(torch, lambda i: g8.replay(), max(reps // LAYERS_PER_GRAPH, 5), 3) * 1e3 / LAYERS_PER_GRAPH
         res[str(bucket)] = {"real_rows": real, "kv_MB": round(int(ctx.sum()) * 4096 / 1e6, 1),
                             "eager_us_per_step": round(eager, 1), "graph_us_per_step": round(graph, 1),
+                            "graph_%d_layers_us_per_step" % LAYERS_PER_GRAPH: round(graph8, 1),
                             "eager_us_one_step": round(eager_one, 1), "graph_us_one_step": round(graph_one, 1)}
-        del g, kc, vc, case
+        del g, g8, kc, vc, case
         torch.cuda.empty_cache()
     return res
 
