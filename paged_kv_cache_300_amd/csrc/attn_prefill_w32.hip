@@ -79,15 +79,22 @@ struct WSrc {
   int64_t kstride, vstride;  // elements between rows (contiguous) or slots (paged)
 };
 
-// One direct-to-LDS load of 16 bytes per lane: lane i's bytes land at `dst` + 16 i.  Written as inline assembly
-// on purpose: the compiler would otherwise make every later LDS read wait for all such loads in flight (it cannot
-// tell the tile being filled from the tiles being read), which would expose a memory round trip per tile.  The
-// tiles are published by an explicit wait for all loads (s_waitcnt 0) and a barrier before they are read.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, const lds_u16* dst) {
+// A wave's share of a tile: four direct-to-LDS loads of 16 bytes per lane, lane i of load k landing at
+// `dst` + 1024 k + 16 i.  The immediate offset 1024 k moves both the LDS destination and the global address, so
+// the lane offsets off[k] are given less 1024 k (the bounds check covers the whole offset).  Written as inline
+// assembly on purpose: the compiler would otherwise make every later LDS read wait for all such loads in flight
+// (it cannot tell the tile being filled from the tiles being read), which would expose a memory round trip per
+// tile.  The tiles are published by an explicit wait for all loads (s_waitcnt 0) and a barrier before they are
+// read.
+__device__ __forceinline__ void dma16x4(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[4], const lds_u16* dst) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(dst)));
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_mov_b32 m0, %4\n\t"
+               "buffer_load_dwordx4 %0, %5, 0 offen lds\n\t"
+               "buffer_load_dwordx4 %1, %5, 0 offen offset:1024 lds\n\t"
+               "buffer_load_dwordx4 %2, %5, 0 offen offset:2048 lds\n\t"
+               "buffer_load_dwordx4 %3, %5, 0 offen offset:3072 lds"
                :
-               : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0)
+               : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(m0), "s"(rs)
                : "m0");
 }
 
@@ -106,11 +113,10 @@ struct TileRef {
 __device__ __forceinline__ void dma_rows(const uint16_t* head, int64_t stride, TileRef ref, lds_u16* tile, int w,
                                          const uint32_t (&off)[4]) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + ref.row * stride, uint32_t(ref.rows) * uint32_t(stride) * 2u);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) dma16(rs, off[k], 0u, tile + (w * 16 + k * 4) * WROW);
+  dma16x4(rs, off, tile + w * 16 * WROW);
 }
 
-// Byte offsets (from a tile's first row) of this lane's chunk in each of its wave's four 4-row loads: row
+// Lane offsets of this lane's chunk in each of its wave's four 4-row loads (see dma16x4): row
 // r = 16 w + 4 k + lane / 16, chunk (lane % 16) ^ swz(r).  The swizzles only look at r % 16 = 4 k + lane / 16.
 template <bool IS_V>
 __device__ __forceinline__ void dma_offsets(int64_t stride, int w, int lane, uint32_t (&off)[4]) {
@@ -118,7 +124,8 @@ __device__ __forceinline__ void dma_offsets(int64_t stride, int w, int lane, uin
   for (int k = 0; k < 4; ++k) {
     const int r = w * 16 + k * 4 + (lane >> 4);
     const int c = (lane & 15) ^ (IS_V ? swz_v(r) : swz_k(r));
-    off[k] = uint32_t(r) * uint32_t(stride) * 2u + uint32_t(c) * 16u;
+    // less the immediate offset 1024 k of load k (row r >= 4 k and a row is at least 256 bytes: never negative)
+    off[k] = uint32_t(r) * uint32_t(stride) * 2u + uint32_t(c) * 16u - uint32_t(k) * 1024u;
   }
 }
 
