@@ -6,20 +6,22 @@
 //
 // How (FlashAttention tiling and online softmax [P2 §5.2], shaped for the gfx950 SIMD):
 //  * A work-group owns 64 query tokens of one sequence and one kv head with both query heads that read it; its 4
-//    waves own 32 tokens x 1 head each.  Two work-groups share a CU (80 KB of LDS each), so every SIMD runs two
-//    waves: while one takes its exponentials the other keeps the matrix core busy.  32x32x16 products matter
-//    there: from a single wave a chain of 16x16x32 products reaches about half the matrix-core rate (measured),
-//    a chain of 32x32x16 products about 85 %, so the matrix core stays fed while the other wave is in its vector
-//    phase.
+//    waves own 32 tokens x 1 head each.  Three work-groups share a CU (48 KB of LDS and at most 168 VGPRs each), so
+//    every SIMD runs three waves: while one takes its exponentials the others keep the matrix core busy.  32x32x16
+//    products matter there: from a single wave a chain of 16x16x32 products falls well short of the matrix-core
+//    rate, a chain of 32x32x16 products does not, so the matrix core keeps issuing while another wave is in its
+//    vector phase.
 //  * Scores are transposed, S^T = K Q^T: Q^T (the B operand) stays in registers; lane (j, half) of a 32x32 block
 //    holds 16 keys of query j, so P^T feeds O^T = V^T P^T straight from registers (the contraction order of the
 //    keys is permuted alike on both operands), and V^T comes from LDS through the transposing ds_read_b64_tr_b16.
 //  * K/V tiles of 64 keys reach LDS by direct-to-LDS buffer loads (no staging registers): lane i of a load lands
 //    at 16 i bytes past the wave's base, so each lane fetches the global chunk that the row's swizzle puts there.
 //    Rows past the end of the keys read as zeros (buffer bounds).  K rows are swizzled by r & 15 and V rows by
-//    4 (r & 3), which makes the 16-byte K reads and the transposing V reads free of bank conflicts.  K tiles
-//    rotate over three buffers and V tiles over two; each step issues the loads of K two tiles ahead and V one
-//    tile ahead, and waits for them (with one barrier) at its end.
+//    4 (r & 3), which makes the 16-byte K reads and the transposing V reads free of bank conflicts.  Two K
+//    buffers and one V buffer: in step kt the K loads of tile kt + 2 go into K tile kt's buffer once every wave
+//    has formed its last scores from it (barrier A, which also waits for the loads in flight), and the V loads of
+//    tile kt + 1 into the V buffer once every wave has finished its P V products (barrier B).  The waits this
+//    leaves are covered by the CU's other two work-groups.
 //  * Per tile, software-pipelined in two halves of 32 keys: the scores of the next half are formed on the matrix
 //    core while the vector unit takes the exponentials of the current half, then O += P V of the current half runs
 //    while the next half's mask and row maxima are reduced.  The online-softmax reference maximum moves only when
@@ -50,7 +52,7 @@ __device__ __forceinline__ u32x2 ds_read_tr16_l(const lds_u16* p) {
 
 constexpr int WROW = 128;          // LDS row: 128 bf16 = 256 B of 16 swizzled 16-byte chunks
 constexpr int WTILE = BN * WROW;   // one K or V tile: 64 keys, 16 KB
-constexpr int NBUF = 5;            // K0, K1, K2, V0, V1
+constexpr int NBUF = 3;            // K0, K1, V
 #ifndef PKV_W32_CHUNK
 #define PKV_W32_CHUNK 4
 #endif
@@ -200,7 +202,7 @@ __device__ __forceinline__ float max_blk(const f32x16_t& x, float c) {
 constexpr int kChunkSeqs = PKV_W32_CHUNK;
 
 template <int MODE>
-__global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p, PlanList plan, int batch) {
+__global__ void __launch_bounds__(256, 3) prefill_w32_kernel(PrefillKernelArgs p, PlanList plan, int batch) {
   int kvh, b, t;
   kvh = int(blockIdx.x % unsigned(p.num_kv_heads));
   const int rank = int(blockIdx.x / unsigned(p.num_kv_heads));
@@ -218,7 +220,7 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
   const SeqGeom g = seq_geom(p, b);
   if (t >= g.T) return;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF][WTILE];  // 80 KB: two work-groups per CU
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NBUF][WTILE];  // 48 KB: three work-groups per CU
   // The wave index is uniform; saying so keeps the LDS bases of the direct-to-LDS loads in scalar registers.
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hn = wave & 1;  // query head kvh * 2 + hn
@@ -264,8 +266,8 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
     dma_offsets<false>(src.kstride, wave, lane, koff);
     dma_offsets<true>(src.vstride, wave, lane, voff);
     lds_u16* const lbase = (lds_u16*)&lds[0][0];
-    auto kbuf = [&](int i) { return lbase + i * WTILE; };
-    auto vbuf = [&](int i) { return lbase + (3 + i) * WTILE; };
+    auto kbuf = [&](int i) { return lbase + (i & 1) * WTILE; };  // K tile kt in buffer kt % 2
+    const lds_u16* const vt = lbase + 2 * WTILE;                   // the V tile
 
     // Scores of block kb of a K tile (the first product starts from zero).
     auto qk = [&](f32x16_t& s, const lds_u16* ktile, int kb) {
@@ -345,11 +347,11 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
       b1 = bt_block(p, b1);
     }
     const TileRef r0 = tile_ref(0, b0);
-    TileRef r1 = tile_ref(1, b1);  // the tile whose V loads the next step issues
+    TileRef r1 = tile_ref(1, b1);  // the tile whose V loads the next barrier B issues
 
     // Prologue: K and V of the first tile and K of the second; scores and maximum of the first block.
     dma_rows(src.khead, src.kstride, r0, kbuf(0), wave, koff);
-    dma_rows(src.vhead, src.vstride, r0, vbuf(0), wave, voff);
+    dma_rows(src.vhead, src.vstride, r0, (lds_u16*)vt, wave, voff);
     if (nt > 1) dma_rows(src.khead, src.kstride, r1, kbuf(1), wave, koff);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -359,22 +361,24 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
     m = fmaxf(m, max_blk(sa, c));
 
     // Step kt (whose first block's scores are in sa): the second block's scores while the first block's weights
-    // are taken, the first block's P V while the second block's maximum is reduced; then the next tile's first
-    // block's scores while the second block's weights are taken, and the second block's P V while the next first
-    // block's maximum is reduced.  `masked`: tile kt + 1 (and so possibly kt) needs the mask.
+    // are taken; then (barrier A: V of tile kt and K of tile kt + 1 have landed, K of tile kt is no longer read)
+    // the K loads of tile kt + 2 into K tile kt's buffer; the first block's P V while the second block's maximum is
+    // reduced; the next tile's first block's scores while the second block's weights are taken, and the second
+    // block's P V while the next first block's maximum is reduced; then (barrier B: V of tile kt is no longer
+    // read) the V loads of tile kt + 1.  `masked`: tile kt + 1 (and so possibly kt) needs the mask.
     auto step = [&](bool masked, auto last_tag, int kt) {
       constexpr bool LAST = decltype(last_tag)::value;
+      u32x4 pb0[2];
+      qk_weights(sb, kbuf(kt), 1, sa, pb0);
+      keep(pb0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // barrier A
+      TileRef r2{};  // tile kt + 2: its K loads now, its V loads at the next step's barrier B
       if (!LAST) {
-        const TileRef r2 = tile_ref(kt + 2, MODE == LOAD_PAGED ? bt_block(p, fk) : 0);
-        if (kt + 2 < nt) dma_rows(src.khead, src.kstride, r2, kbuf((kt + 2) % 3), wave, koff);
-        dma_rows(src.vhead, src.vstride, r1, vbuf((kt + 1) & 1), wave, voff);
-        r1 = r2;
+        r2 = tile_ref(kt + 2, MODE == LOAD_PAGED ? bt_block(p, fk) : 0);
+        if (kt + 2 < nt) dma_rows(src.khead, src.kstride, r2, kbuf(kt), wave, koff);
         if constexpr (MODE == LOAD_PAGED) fk = bt_fetch(p, bt_rs, kt + 3);
       }
-      const lds_u16* vt = vbuf(kt & 1);
-      u32x4 pb0[2];
-      qk_weights(sb, kbuf(kt % 3), 1, sa, pb0);
-      keep(pb0);
       if (masked) {
         asm volatile("");  // keeps the branch: the mask is not applied to tiles that need none
         mask_blk(sb, lim - (kt * BN + 32 + 4 * half));
@@ -383,7 +387,7 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
       decide(sb);
       u32x4 pb1[2];
       if constexpr (!LAST) {
-        qk_weights(sa, kbuf((kt + 1) % 3), 0, sb, pb1);
+        qk_weights(sa, kbuf(kt + 1), 0, sb, pb1);
         keep(pb1);
         if (masked) {
           asm volatile("");
@@ -391,8 +395,9 @@ __global__ void __launch_bounds__(256, 2) prefill_w32_kernel(PrefillKernelArgs p
         }
         pv(vt, 1, pb1);
         decide(sa);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        __syncthreads();  // barrier B
+        dma_rows(src.vhead, src.vstride, r1, (lds_u16*)vt, wave, voff);
+        r1 = r2;
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) weight(sb, 2 * i, pb1);
