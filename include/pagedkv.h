@@ -144,11 +144,14 @@ int kv_store_qk_norm_rope(const void* q, int64_t q_stride, const void* k, int64_
  * max_seqlen_q must be >= every Lq (rows beyond it are not computed); max_seqlen_k is accepted for
  *   signature parity with the pages' call and only checked to be >= 0.
  * workspace: NULL, or device memory of at least attn_prefill_workspace_bytes(...) bytes (contents on
- *   entry do not matter).  With it the bf16 head_dim-128 kernel runs a one-work-group planner that lists
- *   the query tiles longest first, so that the rows with the most keys (long cached prefixes, non-causal
- *   rows) start first and short ones fill the tail; without it the tiles are launched latest-first, which
- *   is the same order for causal attention over a step's own tokens (there the workspace is not used).
- *   Results do not depend on the order.
+ *   entry do not matter).  With it the bf16 head_dim-128 kernels run a one-work-group planner.  For GQA
+ *   groups of 2 it cuts every query tile whose chain of key tiles is longer than the work each resident
+ *   work-group gets into pieces of about that length, lists the pieces longest first, and a second kernel
+ *   merges the pieces' partial softmax states by the exact online-softmax rescaling [P2 §5.2]; when no tile
+ *   is that long it keeps the grid order.  For other groups it lists the query tiles longest first (long
+ *   cached prefixes, non-causal rows), and for causal attention over a step's own tokens it is not used.
+ *   Without it the tiles are launched latest-first.  Results do not depend on the order; a split tile
+ *   differs from an unsplit one only by the rounding of its sums.
  * Unspecified (but in-bounds) results: query rows past num_q_tokens are skipped; key rows past
  *   num_k_rows and block-table entries outside [0, num_blocks) give unspecified values without any
  *   out-of-bounds access.
@@ -163,7 +166,10 @@ int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t 
 
 /*
  * attn_prefill_workspace_bytes -- bytes of device workspace attn_prefill_varlen can use for these sizes
- * (0: it takes none): a count and one (sequence, query tile) entry per possible query tile.
+ * (0: it takes none): a header, one 32-byte entry per possible query tile or piece, and room for the
+ * partial states of split query tiles -- 2 * (W / num_kv_heads + 1) states of 68 KiB per kv head, W the
+ * work-groups the current device holds at once (about 107 MB on a 256-CU MI355X).  Sized for the device
+ * current at the call; a smaller workspace is refused with -3.
  */
 size_t attn_prefill_workspace_bytes(int32_t batch, int32_t num_q_tokens, int32_t max_seqlen_q, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype);

@@ -248,7 +248,7 @@ int attn_prefill_varlen(const void* q, int64_t q_stride, const void* k, int64_t 
       const size_t need = pkv::prefill_workspace_bytes(batch, num_q_tokens, max_seqlen_q, num_kv_heads);
       if (need > 0 && workspace_bytes < need)
         return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-      if (need == 0 || !pkv::prefill_wants_order(a)) workspace = nullptr;
+      if (need == 0 || !pkv::prefill_wants_plan(a)) workspace = nullptr;
     }
     return hip_status(pkv::launch_prefill_bf16(a, workspace, workspace_bytes, stream),
                       "attn_prefill_varlen launch");

@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -708,9 +709,15 @@ struct PlanArgs {
   int batch;
   int buckets;   // key-tile counts 1 .. buckets (larger counts share the last), from max_seqlen_k
   int unit_cap;  // list capacity; units past it are dropped (the host sizes it from num_q_tokens)
-  int2* list;    // [unit_cap] (sequence, query tile), longest first
-  int* count;    // number of listed units
+  void* list;    // [unit_cap] (sequence, query tile) entries, longest first
+  int* count;    // number of listed units; the 32x32 form also writes count[1] = 0 splits, count[2] = 1 (listed)
 };
+
+// A listed unit: (sequence, tile) for the 16x16 kernels, a whole-unit piece for the 32x32 kernel.
+__device__ __forceinline__ void put_unit(int2* list, int i, int b, int t) { list[i] = make_int2(b, t); }
+__device__ __forceinline__ void put_unit(PrefillPiece* list, int i, int b, int t) {
+  list[i] = PrefillPiece{b, t, 0, -1, -1, 0, 0, 0};
+}
 
 // Exclusive prefix sum of a[0 .. n) in place; returns the total.  All threads call it.
 __device__ int block_exclusive_scan(int* a, int n, int* chunk) {
@@ -738,6 +745,7 @@ __device__ int block_exclusive_scan(int* a, int n, int* chunk) {
   return total;
 }
 
+template <typename Entry>
 __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(PrefillKernelArgs p, PlanArgs pa) {
   __shared__ int uoff[PLAN_MAX_BATCH + 1];  // first unit of each sequence
   __shared__ int sc0[PLAN_MAX_BATCH], snk[PLAN_MAX_BATCH];
@@ -777,9 +785,137 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_plan_kernel(PrefillKerne
   for (int u = tid; u < units; u += PLAN_THREADS) {
     int b, t;
     const int slot = atomicAdd(&start[locate(u, b, t)], 1);
-    pa.list[slot] = make_int2(b, t);
+    put_unit(static_cast<Entry*>(pa.list), slot, b, t);
   }
-  if (tid == 0) *pa.count = units;
+  if (tid == 0) {
+    pa.count[0] = units;
+    if constexpr (!std::is_same<Entry, int2>::value) {
+      pa.count[1] = 0;
+      pa.count[2] = 1;
+    }
+  }
+}
+
+// Splitting planner for the 32x32 kernel.  A query tile's keys are a chain of key tiles that one work-group walks
+// in order; when the longest chains are much longer than the share of work each resident work-group gets, they
+// set the kernel's length.  With W the batch's key tiles over all units and S the work-groups the device holds at
+// once, P = max(kPieceMin, ceil(W Hkv / S)) is that share: a unit of nk > P key tiles is cut into ceil(nk / P)
+// pieces of (nearly) equal length whose partial softmax states the merge kernel combines, and the pieces are listed
+// longest first.  Bounds that size the workspace: every split unit has nk > P, so there are fewer than W / P <= S /
+// Hkv of them, the extra pieces number fewer than W / P, and the partial slots (pieces of split units) fewer than
+// 2 S / Hkv.  The host runs it only where whole units cannot fill half of the resident work-groups (few query
+// tiles over long keys: a chunk of new tokens on a long cached prefix); elsewhere the merge's extra launch and
+// partial-state traffic cost more than the balance gains, and the units run whole.
+constexpr int kPieceMin = 16;
+
+struct SplitPlanArgs {
+  int batch;
+  int buckets;    // piece lengths 1 .. buckets (longer ones share the last)
+  int unit_cap;   // units the workspace was sized for (units past it are dropped)
+  int list_cap;   // pieces that fit the list
+  int split_cap;  // split units that fit the split list (their partial slots: 2 split_cap)
+  int slots;      // work-groups resident at once
+  PrefillPiece* list;
+  PrefillSplit* splits;
+  int* hdr;       // [0] pieces listed, [1] split units, [2] 1: listed order, 0: grid order
+};
+
+__global__ void __launch_bounds__(PLAN_THREADS) prefill_split_plan_kernel(PrefillKernelArgs p, SplitPlanArgs pa) {
+  __shared__ int uoff[PLAN_MAX_BATCH + 1];  // first unit of each sequence
+  __shared__ int sc0[PLAN_MAX_BATCH], snk[PLAN_MAX_BATCH];
+  __shared__ int start[PLAN_BUCKETS];       // bucket i holds pieces of `buckets` - i key tiles (clamped)
+  __shared__ int chunk[PLAN_THREADS];
+  __shared__ unsigned long long s_w;
+  __shared__ int s_max, s_pieces, s_split, s_parts, s_sid, s_pbase;
+  const int tid = threadIdx.x, nb = pa.batch, nbk = pa.buckets;
+  for (int b = tid; b < nb; b += PLAN_THREADS) {
+    const SeqGeom g = seq_geom(p, b);
+    uoff[b] = min(g.T, p.max_tiles);  // rows past max_seqlen_q are not computed
+    sc0[b] = g.c0;
+    snk[b] = g.NKe;
+  }
+  for (int i = tid; i < nbk; i += PLAN_THREADS) start[i] = 0;
+  if (tid == 0) {
+    s_w = 0;
+    s_max = s_pieces = s_split = s_parts = s_sid = s_pbase = 0;
+  }
+  __syncthreads();
+  const int units = min(block_exclusive_scan(uoff, nb, chunk), pa.unit_cap);
+  if (tid == 0) uoff[nb] = units;
+  __syncthreads();
+  // Unit u -> (sequence, tile) and its key-tile count.
+  auto locate = [&](int u, int& b, int& t) {
+    int lo = 0, hi = nb - 1;  // last b with uoff[b] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uoff[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    t = u - uoff[lo];
+    return min(max(t + 1 + sc0[lo], 1), snk[lo]);
+  };
+  {
+    unsigned long long w = 0;
+    int mx = 0;
+    for (int u = tid; u < units; u += PLAN_THREADS) {
+      int b, t;
+      const int nk = locate(u, b, t);
+      w += unsigned(nk);
+      mx = max(mx, nk);
+    }
+    atomicAdd(&s_w, w);
+    atomicMax(&s_max, mx);
+  }
+  __syncthreads();
+  const unsigned long long share = (s_w * unsigned(p.num_kv_heads) + unsigned(pa.slots) - 1) / unsigned(pa.slots);
+  const int P = int(min(max(share, (unsigned long long)kPieceMin), (unsigned long long)INT32_MAX));
+  auto npieces = [&](int nk) { return nk > P ? (nk + P - 1) / P : 1; };
+  auto bucket = [&](int len) { return nbk - min(len, nbk); };
+  bool split = true;
+  {  // counting pass
+    for (int u = tid; u < units; u += PLAN_THREADS) {
+      int b, t;
+      const int nk = locate(u, b, t), np = npieces(nk);
+      for (int k = 0; k < np; ++k) atomicAdd(&start[bucket((k + 1) * nk / np - k * nk / np)], 1);
+      atomicAdd(&s_pieces, np);
+      if (np > 1) {
+        atomicAdd(&s_split, 1);
+        atomicAdd(&s_parts, np);
+      }
+    }
+    __syncthreads();
+    // The bounds above guarantee these fit; the check keeps an inconsistent sizing from writing past the lists.
+    split = s_pieces <= pa.list_cap && s_split <= pa.split_cap && s_parts <= 2 * pa.split_cap;
+  }
+  if (!split) {
+    if (tid == 0) {
+      pa.hdr[0] = 0;
+      pa.hdr[1] = 0;
+      pa.hdr[2] = 0;
+    }
+    return;
+  }
+  block_exclusive_scan(start, nbk, chunk);
+  for (int u = tid; u < units; u += PLAN_THREADS) {
+    int b, t;
+    const int nk = locate(u, b, t), np = npieces(nk);
+    int pbase = -1;
+    if (np > 1) {
+      const int sid = atomicAdd(&s_sid, 1);
+      pbase = atomicAdd(&s_pbase, np);
+      pa.splits[sid] = PrefillSplit{b, t, np, pbase};
+    }
+    for (int k = 0; k < np; ++k) {
+      const int k0 = k * nk / np, k1 = (k + 1) * nk / np;
+      const int pos = atomicAdd(&start[bucket(k1 - k0)], 1);
+      pa.list[pos] = PrefillPiece{b, t, k0, k1, np > 1 ? pbase + k : -1, 0, 0, 0};
+    }
+  }
+  if (tid == 0) {
+    pa.hdr[0] = s_pieces;
+    pa.hdr[1] = s_split;
+    pa.hdr[2] = 1;
+  }
 }
 
 template <int G, int H, int MODE>
@@ -805,16 +941,17 @@ template <int G, int H>
 hipError_t launch_g(const PrefillKernelArgs& p, int batch, int mode, const PlanArgs* plan, hipStream_t stream) {
   constexpr int NT = 64 * TOKEN_WAVES * (G / H);
   if (plan) {
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, p, *plan);
+    hipLaunchKernelGGL(prefill_plan_kernel<int2>, dim3(1), dim3(PLAN_THREADS), 0, stream, p, *plan);
     const dim3 grid(unsigned(plan->unit_cap) * unsigned(p.num_kv_heads));
+    const int2* list = static_cast<const int2*>(plan->list);
     if (mode == LOAD_CONTIG)
-      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_CONTIG>), grid, dim3(NT), 0, stream, p, plan->list,
+      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_CONTIG>), grid, dim3(NT), 0, stream, p, list,
                          plan->count);
     else if (mode == LOAD_PAGED)
-      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_PAGED>), grid, dim3(NT), 0, stream, p, plan->list,
+      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_PAGED>), grid, dim3(NT), 0, stream, p, list,
                          plan->count);
     else
-      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_ROWS>), grid, dim3(NT), 0, stream, p, plan->list,
+      hipLaunchKernelGGL((prefill_ordered_kernel<G, H, LOAD_ROWS>), grid, dim3(NT), 0, stream, p, list,
                          plan->count);
     return hipGetLastError();
   }
@@ -852,12 +989,63 @@ bool prefill_fast_strides_ok(int64_t k_stride, int64_t v_stride) {
   return int64_t(BN) * max(k_stride, v_stride) * 2 < (int64_t(1) << 31);
 }
 
-size_t prefill_workspace_bytes(int batch, int num_q_tokens, int max_seqlen_q, int num_kv_heads) {
-  if (batch < 1 || batch > PLAN_MAX_BATCH || num_kv_heads < 1) return 0;
-  const int64_t cap = unit_cap(batch, num_q_tokens, max_seqlen_q);
-  if (cap < 1 || cap * num_kv_heads > INT32_MAX) return 0;
-  return PLAN_HEADER_BYTES + size_t(cap) * sizeof(int2);
+namespace {
+
+// Work-groups of the 32x32 kernel the current device holds at once (cached per device; several host threads may
+// ask at once and store equal values).
+int w32_slots() {
+  static std::atomic<int> cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (const int v = cached[dev].load(std::memory_order_relaxed); v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  const int v = cus * kW32PerCU;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace of the planners: a header, then the piece list (the 16x16 planner's (sequence, tile) list uses its
+// start), the split list and the partial states of the pieces of split units.
+struct PlanLayout {
+  int unit_cap, split_cap, list_cap;
+  size_t list, splits, parts, total;
+};
+PlanLayout plan_layout(int batch, int num_q_tokens, int max_seqlen_q, int num_kv_heads) {
+  PlanLayout L{};
+  const int64_t cap = unit_cap(batch, num_q_tokens, max_seqlen_q);
+  if (batch < 1 || batch > PLAN_MAX_BATCH || num_kv_heads < 1 || cap < 1) return L;
+  const int split_cap = w32_slots() / num_kv_heads + 1;
+  if ((cap + split_cap) * num_kv_heads > INT32_MAX) return L;
+  L.unit_cap = int(cap);
+  L.split_cap = split_cap;
+  L.list_cap = int(cap) + split_cap;
+  L.list = PLAN_HEADER_BYTES;
+  L.splits = align256(L.list + size_t(L.list_cap) * sizeof(PrefillPiece));
+  L.parts = align256(L.splits + size_t(split_cap) * sizeof(PrefillSplit));
+  L.total = L.parts + size_t(2 * split_cap) * size_t(num_kv_heads) * kPartialFloat4 * sizeof(f32x4_t);
+  return L;
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int batch, int num_q_tokens, int max_seqlen_q, int num_kv_heads) {
+  return plan_layout(batch, num_q_tokens, max_seqlen_q, num_kv_heads).total;
+}
+
+bool prefill_wants_split(const AttnArgs& a) {
+  // 32x32 kernel: the (sequence, query tile) units cannot fill half of the resident work-groups, and some unit
+  // may be longer than the shortest piece.  With at most U units the longest chain is at least S / (U Hkv) times
+  // the even share, so at U Hkv <= S / 2 splitting at least halves the kernel's critical path.
+  const int group = a.num_q_heads / a.num_kv_heads;
+  if (!prefill_w32_supported(group, load_mode(a), a.scale)) return false;
+  const int64_t units = unit_cap(a.batch, a.num_q_tokens, a.max_seqlen_q);
+  return units * a.num_kv_heads * 2 <= w32_slots() && (int64_t(std::max(a.max_seqlen_k, 0)) + BN - 1) / BN > kPieceMin;
+}
+
+bool prefill_wants_plan(const AttnArgs& a) { return prefill_wants_split(a) || prefill_wants_order(a); }
 
 bool prefill_wants_order(const AttnArgs& a) {
   // Cached prefixes of different lengths or non-causal rows: a query tile's work is not given by its index.
@@ -899,24 +1087,50 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, void* workspace, size_t worksp
   const int group = a.num_q_heads / a.num_kv_heads;
   PlanArgs plan{};
   const PlanArgs* planp = nullptr;
-  const size_t need = prefill_workspace_bytes(a.batch, a.num_q_tokens, a.max_seqlen_q, a.num_kv_heads);
-  if (workspace && need > 0 && workspace_bytes >= need) {
+  const PlanLayout L = plan_layout(a.batch, a.num_q_tokens, a.max_seqlen_q, a.num_kv_heads);
+  const bool planned = workspace && L.total > 0 && workspace_bytes >= L.total;
+  char* const ws = static_cast<char*>(workspace);
+  const int buckets = int(std::min<int64_t>(PLAN_BUCKETS, (int64_t(std::max(a.max_seqlen_k, 0)) + BN - 1) / BN + 1));
+  if (planned) {
     plan.batch = a.batch;
-    plan.buckets = int(std::min<int64_t>(PLAN_BUCKETS, (int64_t(std::max(a.max_seqlen_k, 0)) + BN - 1) / BN + 1));
-    plan.unit_cap = int(unit_cap(a.batch, a.num_q_tokens, a.max_seqlen_q));
-    plan.count = static_cast<int*>(workspace);
-    plan.list = reinterpret_cast<int2*>(static_cast<char*>(workspace) + PLAN_HEADER_BYTES);
+    plan.buckets = buckets;
+    plan.unit_cap = L.unit_cap;
+    plan.count = reinterpret_cast<int*>(ws);
+    plan.list = ws + L.list;
     planp = &plan;
   } else if (p.max_tiles > 65535) {
     return hipErrorInvalidConfiguration;
   }
 #ifndef PKV_PREFILL_16X16_ONLY
   if (prefill_w32_supported(group, mode, a.scale)) {
-    const PlanList pl{planp ? planp->list : nullptr, planp ? planp->count : nullptr};
-    if (planp) hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, p, *planp);
-    return launch_prefill_w32(p, a.batch, mode, pl, planp ? planp->unit_cap : 0, stream);
+    if (!planned) return launch_prefill_w32(p, a.batch, mode, PieceList{}, 0, 0, stream);
+    PieceList pl{reinterpret_cast<PrefillPiece*>(ws + L.list), reinterpret_cast<int*>(ws),
+                 reinterpret_cast<PrefillSplit*>(ws + L.splits), reinterpret_cast<f32x4_t*>(ws + L.parts)};
+    if (!prefill_wants_split(a)) {
+      if (!prefill_wants_order(a)) return launch_prefill_w32(p, a.batch, mode, PieceList{}, 0, 0, stream);
+      hipLaunchKernelGGL(prefill_plan_kernel<PrefillPiece>, dim3(1), dim3(PLAN_THREADS), 0, stream, p, plan);
+      return launch_prefill_w32(p, a.batch, mode, pl, L.unit_cap, 0, stream);
+    }
+    SplitPlanArgs sp{};
+    sp.batch = a.batch;
+    sp.buckets = buckets;
+    sp.unit_cap = L.unit_cap;
+    sp.list_cap = L.list_cap;
+    sp.split_cap = L.split_cap;
+    sp.slots = std::max(1, std::min(w32_slots(), (L.split_cap - 1) * a.num_kv_heads));
+    sp.list = reinterpret_cast<PrefillPiece*>(ws + L.list);
+    sp.splits = reinterpret_cast<PrefillSplit*>(ws + L.splits);
+    sp.hdr = reinterpret_cast<int*>(ws);
+    hipLaunchKernelGGL(prefill_split_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, p, sp);
+    // Grid: the longer of the listed pieces and the grid order (the planner's fallback when its lists would
+    // overflow, which the workspace bounds rule out).
+    const int64_t grid_units = std::max<int64_t>(L.list_cap, int64_t(a.batch) * p.max_tiles);
+    if (grid_units > INT32_MAX) return hipErrorInvalidConfiguration;
+    return launch_prefill_w32(p, a.batch, mode, pl, int(grid_units), L.split_cap, stream);
   }
 #endif
+  if (planp && !prefill_wants_order(a)) planp = nullptr;
+  if (!planp && p.max_tiles > 65535) return hipErrorInvalidConfiguration;
   return group == 1   ? launch_g<1, 1>(p, a.batch, mode, planp, stream)
          : group == 2 ? launch_g<2, PKV_PREFILL_H2>(p, a.batch, mode, planp, stream)
                       : launch_g<4, 2>(p, a.batch, mode, planp, stream);

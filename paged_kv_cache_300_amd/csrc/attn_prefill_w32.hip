@@ -58,17 +58,43 @@ __device__ __forceinline__ void dma_rows(const uint16_t* head, int64_t stride, T
 // kChunkSeqs sequences, which its L2 holds, instead of one tile each of every sequence.
 constexpr int kChunkSeqs = PKV_W32_CHUNK;
 
+// 1 / l of a token row: the lane's sum l covers its 16 keys of each block, its partner lane (^ 32) the other 16
+// (0 for a row that saw no key).
+__device__ __forceinline__ float row_inverse(float l) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+  const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  return lt > 0.f ? 1.f / lt : 0.f;
+}
+// O block db of one token row of one query head, times inv, in bf16: lane (j, half) holds dims
+// 32 db + 8 (r / 4) + 4 half + r % 4 of the row.
+__device__ __forceinline__ void write_block(const PrefillKernelArgs& p, int64_t row, int head, int half, int db,
+                                            const f32x16_t& o, float inv) {
+  uint16_t* orow = p.out + (row * p.num_q_heads + head) * HD + 32 * db + 4 * half;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    u32x2 w;
+    w.x = pack_bf16x2(o[4 * v] * inv, o[4 * v + 1] * inv);
+    w.y = pack_bf16x2(o[4 * v + 2] * inv, o[4 * v + 3] * inv);
+    *reinterpret_cast<u32x2*>(orow + 8 * v) = w;
+  }
+}
+
 template <int MODE>
-__global__ void __launch_bounds__(256, 3) prefill_w32_kernel(PrefillKernelArgs p, PlanList plan, int batch) {
+__global__ void __launch_bounds__(256, kW32PerCU) prefill_w32_kernel(PrefillKernelArgs p, PieceList plan, int batch) {
   int kvh, b, t;
+  int kt0 = 0, kt1 = -1, pslot = -1;  // key tiles [kt0, kt1) (kt1 < 0: all of the unit's); partial slot or -1
   kvh = int(blockIdx.x % unsigned(p.num_kv_heads));
   const int rank = int(blockIdx.x / unsigned(p.num_kv_heads));
-  if (plan.list) {
-    if (rank >= *plan.count) return;
-    const int2 u = plan.list[rank];
-    b = u.x;
-    t = u.y;
+  if (plan.list && plan.hdr[2]) {
+    if (rank >= plan.hdr[0]) return;
+    const PrefillPiece u = plan.list[rank];
+    b = u.b;
+    t = u.t;
+    kt0 = u.kt0;
+    kt1 = u.kt1;
+    pslot = u.pslot;
   } else {
+    if (int64_t(rank) >= int64_t(batch) * p.max_tiles) return;
     const int chunk = rank / (kChunkSeqs * p.max_tiles), r = rank - chunk * kChunkSeqs * p.max_tiles;
     const int nseq = min(kChunkSeqs, batch - chunk * kChunkSeqs);
     b = chunk * kChunkSeqs + r % nseq;
@@ -88,7 +114,9 @@ __global__ void __launch_bounds__(256, 3) prefill_w32_kernel(PrefillKernelArgs p
   const int tok = t0 + 32 * (wave >> 1) + j;  // this lane's query token (column of every 32x32 block)
   const int lim = p.causal ? min(Lk - Lq + tok, Lk - 1) : Lk - 1;
   const bool qok = tok < Lq && g.q_start + tok < p.num_q_tokens;
-  const int nt = unit_tiles(g, t);
+  // This piece's key tiles (a unit's are [0, unit_tiles)); a planned range is clamped to the unit's.
+  const int nt = kt1 < 0 ? unit_tiles(g, t) : min(kt1, unit_tiles(g, t));
+  kt0 = min(max(kt0, 0), nt - 1);
   int kt_mask = Lk / BN;  // tiles >= kt_mask need the mask
   if (p.causal) kt_mask = min(kt_mask, qpos0 + 1 > 0 ? (qpos0 + 1) / BN : 0);
 
@@ -197,24 +225,24 @@ __global__ void __launch_bounds__(256, 3) prefill_w32_kernel(PrefillKernelArgs p
         kBufferFlags);
     int fk = 0, b0 = 0, b1 = 0;
     if constexpr (MODE == LOAD_PAGED) {
-      b0 = bt_fetch(p, bt_rs, 0);
-      b1 = bt_fetch(p, bt_rs, 1);
-      fk = bt_fetch(p, bt_rs, 2);
+      b0 = bt_fetch(p, bt_rs, kt0);
+      b1 = bt_fetch(p, bt_rs, kt0 + 1);
+      fk = bt_fetch(p, bt_rs, kt0 + 2);
       b0 = bt_block(p, b0);
       b1 = bt_block(p, b1);
     }
-    const TileRef r0 = tile_ref(0, b0);
-    TileRef r1 = tile_ref(1, b1);  // the tile whose V loads the next barrier B issues
+    const TileRef r0 = tile_ref(kt0, b0);
+    TileRef r1 = tile_ref(kt0 + 1, b1);  // the tile whose V loads the next barrier B issues
 
     // Prologue: K and V of the first tile and K of the second; scores and maximum of the first block.
-    dma_rows(src.khead, src.kstride, r0, kbuf(0), wave, koff);
+    dma_rows(src.khead, src.kstride, r0, kbuf(kt0), wave, koff);
     dma_rows(src.vhead, src.vstride, r0, (lds_u16*)vt, wave, voff);
-    if (nt > 1) dma_rows(src.khead, src.kstride, r1, kbuf(1), wave, koff);
+    if (kt0 + 1 < nt) dma_rows(src.khead, src.kstride, r1, kbuf(kt0 + 1), wave, koff);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16_t sa, sb;  // scores of the tile's first block (sa) and second block (sb)
-    qk(sa, kbuf(0), 0);
-    if (0 >= kt_mask) mask_blk(sa, lim - 4 * half);
+    qk(sa, kbuf(kt0), 0);
+    if (kt0 >= kt_mask) mask_blk(sa, lim - (kt0 * BN + 4 * half));
     m = fmaxf(m, max_blk(sa, c));
 
     // Step kt (whose first block's scores are in sa): the second block's scores while the first block's weights
@@ -263,26 +291,68 @@ __global__ void __launch_bounds__(256, 3) prefill_w32_kernel(PrefillKernelArgs p
     };
     const std::integral_constant<bool, false> no;
     const std::integral_constant<bool, true> yes;
-    for (int kt = 0; kt + 1 < nt; ++kt) step(kt + 1 >= kt_mask, no, kt);
+    for (int kt = kt0; kt + 1 < nt; ++kt) step(kt + 1 >= kt_mask, no, kt);
     step(true, yes, nt - 1);
   }
 
-  // Normalise and write: the lane's sum covers its 16 keys of each block, its partner lane (^ 32) the other 16.
-  // Lane (j, half) holds dims 32 db + 8 (r / 4) + 4 half + r % 4 of token `tok`.
+  // A piece of a split unit hands its state (O, m, l) on to the merge kernel, every lane whatever its row (plain
+  // stores: the merge, launched next, reads them while they are still in the caches).
+  if (pslot >= 0) {
+    f32x4_t* dst = plan.parts + ((size_t(pslot) * p.num_kv_heads + kvh) * 4 + wave) * (kPartialChunks * 64) + lane;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dst[(4 * db + v) * 64] = f32x4_t{o[db][4 * v], o[db][4 * v + 1], o[db][4 * v + 2], o[db][4 * v + 3]};
+    dst[16 * 64] = f32x4_t{m, l, 0.f, 0.f};
+    return;
+  }
   if (!qok) return;
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-  const float lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  uint16_t* orow = p.out + (int64_t(g.q_start + tok) * p.num_q_heads + kvh * 2 + hn) * HD + 4 * half;
+  const float inv = row_inverse(l);
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db) write_block(p, g.q_start + tok, kvh * 2 + hn, half, db, o[db], inv);
+}
+
+// Merge of the split units: one work-group per (split unit, kv head, 32-dim block db of the output), the lanes laid
+// out as the main kernel's, so each lane combines its own (m, l) and O block of every piece: with M the largest m,
+// O = sum O_i 2^(m_i - M) and l = sum l_i 2^(m_i - M) -- the exact online-softmax rescaling [P2 §5.2 ②] (a piece
+// in which a row saw no key has m = -1e30 and contributes nothing).  The loads of several pieces are in flight at
+// once (the loops are unrolled), so a unit cut into many pieces does not pay one memory round trip per piece.
+__global__ void __launch_bounds__(256) prefill_w32_merge_kernel(PrefillKernelArgs p, PieceList plan) {
+  const int db = int(blockIdx.x & 3u);
+  const int kvh = int((blockIdx.x >> 2) % unsigned(p.num_kv_heads));
+  const int s = int((blockIdx.x >> 2) / unsigned(p.num_kv_heads));
+  if (s >= plan.hdr[1]) return;
+  const PrefillSplit e = plan.splits[s];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 31, half = lane >> 5;
+  const int q_start = p.cu_q[e.b], Lq = max(p.cu_q[e.b + 1] - q_start, 0);
+  const int tok = e.t * BM + 32 * (wave >> 1) + j;
+  const f32x4_t* src = plan.parts + ((size_t(e.pbase) * p.num_kv_heads + kvh) * 4 + wave) * (kPartialChunks * 64) + lane;
+  const size_t piece_stride = size_t(p.num_kv_heads) * 4 * kPartialChunks * 64;
+  float mmax = kMinusBig;
+#pragma unroll 8
+  for (int i = 0; i < e.np; ++i) mmax = fmaxf(mmax, src[i * piece_stride + 16 * 64][0]);
+  f32x16_t o[1];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      u32x2 w;
-      w.x = pack_bf16x2(o[db][4 * v] * inv, o[db][4 * v + 1] * inv);
-      w.y = pack_bf16x2(o[db][4 * v + 2] * inv, o[db][4 * v + 3] * inv);
-      *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * v) = w;
-    }
+  for (int r = 0; r < 16; ++r) o[0][r] = 0.f;
+  float l = 0.f;
+#pragma unroll 4
+  for (int i = 0; i < e.np; ++i) {
+    const f32x4_t* q = src + i * piece_stride;
+    const f32x4_t ml = q[16 * 64];
+    f32x4_t x[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[v] = q[(4 * db + v) * 64];
+    const float f = fast_exp2(ml[0] - mmax);
+    l = fmaf(ml[1], f, l);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[0][4 * v + k] = fmaf(x[v][k], f, o[0][4 * v + k]);
+  }
+  if (tok >= Lq || int64_t(q_start) + tok >= p.num_q_tokens) return;
+  write_block(p, int64_t(q_start) + tok, kvh * 2 + (wave & 1), half, db, o[0], row_inverse(l));
 }
 
 }  // namespace
@@ -291,18 +361,22 @@ bool prefill_w32_supported(int group, int mode, float scale) {
   return group == 2 && (mode == LOAD_CONTIG || mode == LOAD_PAGED) && scale > 0.f;
 }
 
-hipError_t launch_prefill_w32(const PrefillKernelArgs& p, int batch, int mode, PlanList plan, int grid_units,
-                              hipStream_t stream) {
+hipError_t launch_prefill_w32(const PrefillKernelArgs& p, int batch, int mode, PieceList plan, int grid_units,
+                              int split_cap, hipStream_t stream) {
   const dim3 block(256);
   const uint64_t units = plan.list ? uint64_t(grid_units) : uint64_t(batch) * uint64_t(p.max_tiles);
   const uint64_t wgs = units * uint64_t(p.num_kv_heads);
   if (wgs == 0) return hipSuccess;
-  if (wgs > 0xffffffffull) return hipErrorInvalidConfiguration;
+  if (wgs > 0xffffffffull || uint64_t(split_cap) * uint64_t(p.num_kv_heads) * 4u > 0xffffffffull)
+    return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<uint32_t>(wgs));
   if (mode == LOAD_CONTIG)
     hipLaunchKernelGGL(prefill_w32_kernel<LOAD_CONTIG>, grid, block, 0, stream, p, plan, batch);
   else
     hipLaunchKernelGGL(prefill_w32_kernel<LOAD_PAGED>, grid, block, 0, stream, p, plan, batch);
+  if (plan.list && split_cap > 0)
+    hipLaunchKernelGGL(prefill_w32_merge_kernel, dim3(uint32_t(split_cap) * uint32_t(p.num_kv_heads) * 4u), block,
+                       0, stream, p, plan);
   return hipGetLastError();
 }
 

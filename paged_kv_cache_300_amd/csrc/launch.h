@@ -74,10 +74,13 @@ hipError_t launch_decode_store(const DecodeStoreArgs& s, const int32_t* context_
 bool prefill_fast_supported(int head_dim, int group, bool bf16);
 // Contiguous K/V rows: a 64-row tile must span < 2^31 bytes.
 bool prefill_fast_strides_ok(int64_t k_stride, int64_t v_stride);
-// Workspace of the longest-first planner (0: not available for these sizes).
+// Workspace of the planners: the longest-first list, and for the 32x32 kernel the pieces of split query tiles and
+// their partial states (0: not available for these sizes).
 size_t prefill_workspace_bytes(int batch, int num_q_tokens, int max_seqlen_q, int num_kv_heads);
-// Whether the longest-first order can beat the grid's launch order for this call.
+// Whether the longest-first order can beat the grid's launch order for this call (16x16 kernels).
 bool prefill_wants_order(const AttnArgs& a);
+// Whether a workspace can help this call: the longest-first order, or the splitting of long query tiles.
+bool prefill_wants_plan(const AttnArgs& a);
 // workspace == NULL: grid order; else the planner orders the query tiles longest first.
 hipError_t launch_prefill_bf16(const AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -142,14 +142,39 @@ struct PlanList {
   const int* count;
 };
 
+// The splitting planner's output for the 32x32 kernel: work pieces, each the key tiles [kt0, kt1) of one
+// (sequence, query tile) unit, largest first.  pslot >= 0 marks a piece of a split unit, which writes its partial
+// softmax state (O, m, l) to partial slot pslot instead of the output; the merge kernel then combines the pieces
+// of each split unit (splits[i] = its sequence, query tile, piece count and first partial slot).
+struct PrefillPiece {
+  int b, t, kt0, kt1, pslot, pad0, pad1, pad2;
+};
+struct PrefillSplit {
+  int b, t, np, pbase;
+};
+// Partial state of one piece and kv head: per wave of the work-group and lane, 16 float4 of O (chunk 4 db + v holds
+// o[db][4 v .. 4 v + 3]) then one float4 (m, l, 0, 0); chunk-major, so a wave's store of one chunk is 1 KiB
+// contiguous.
+constexpr int kPartialChunks = 17;
+constexpr size_t kPartialFloat4 = size_t(4) * kPartialChunks * 64;  // per (piece, kv head): 4 waves
+
+struct PieceList {
+  const PrefillPiece* list;  // NULL: grid order, no planner
+  const int* hdr;            // [0] pieces listed, [1] split units, [2] 1: listed order, 0: grid order
+  const PrefillSplit* splits;
+  f32x4_t* parts;
+};
+
 }  // namespace pf
 
 // 32x32 MFMA prefill for GQA groups of 2 with contiguous rows or a paged cache whose block size is a power of two
 // >= 64, and a positive softmax scale (attn_prefill_w32.hip).  plan.list == NULL: one work-group per (kv head,
-// sequence, query tile), sequences in chunks with each chunk's latest tiles first; else one per listed unit and kv
-// head (grid_units units).
+// sequence, query tile), sequences in chunks with each chunk's latest tiles first; else one per listed piece and kv
+// head (grid_units pieces at most), followed by the merge of the split units (split_cap of them at most).
 bool prefill_w32_supported(int group, int mode, float scale);
-hipError_t launch_prefill_w32(const pf::PrefillKernelArgs& p, int batch, int mode, pf::PlanList plan, int grid_units,
-                              hipStream_t stream);
+hipError_t launch_prefill_w32(const pf::PrefillKernelArgs& p, int batch, int mode, pf::PieceList plan, int grid_units,
+                              int split_cap, hipStream_t stream);
+// Work-groups of the 32x32 kernel one CU holds at once.
+constexpr int kW32PerCU = 3;
 
 }  // namespace pkv

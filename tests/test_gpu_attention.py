@@ -206,8 +206,10 @@ ORDER_CASES = [
 
 @pytest.mark.parametrize("hq,hkv,lq,prefix,bs,seed", ORDER_CASES)
 def test_prefill_longest_first_order(pkv, hq, hkv, lq, prefix, bs, seed):
-    """Query tiles listed longest first by the planner: same values as the latest-tile-first grid, bit for bit
-    (each tile's arithmetic does not depend on when it runs), and within tolerance of the oracle."""
+    """Query tiles listed longest first by the planner (for GQA groups of 2 also cut into key-range pieces
+    merged afterwards): within tolerance of the oracle, as is the latest-tile-first grid, and the two differ
+    only by rounding (a split tile sums its keys in pieces; a tile's arithmetic does not depend on when it
+    runs)."""
     lk = [a + b for a, b in zip(lq, prefix)]
     case = workloads.make_case(lq, lk, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=bs,
                                num_blocks=sum(math.ceil(c / bs) for c in lk) + 2, dtype="bf16", seed=seed)
@@ -215,7 +217,34 @@ def test_prefill_longest_first_order(pkv, hq, hkv, lq, prefix, bs, seed):
     out, *_ = _run_step(pkv, case, paged=True, order=True)
     _check_attention(case, out)
     ref, *_ = _run_step(pkv, case, paged=True, order=False)
-    assert torch.equal(out, ref)
+    _check_attention(case, ref)
+    # one bf16 rounding step of the value (2^-8 relative) plus float32 summation noise
+    torch.testing.assert_close(out.float(), ref.float(), rtol=2.0 ** -7, atol=1e-3)
+
+
+SPLIT_CASES = [
+    # (lq, prefix, paged, block_size): too few query tiles to fill the GPU, over key ranges far longer than the
+    # work each resident work-group gets, so the planner cuts them into pieces (causal diagonal tiles in the last
+    # piece, cached prefixes spanning many pieces, short rows beside them)
+    ([2000, 5, 64], [0, 0, 0], False, 256),
+    ([700, 130, 1], [5000, 3000, 7000], True, 256),
+    ([1100, 64, 65], [2300, 4100, 0], True, 64),
+    ([64], [20000], True, 256),  # one chunk of new tokens on a long cached prefix
+]
+
+
+@pytest.mark.parametrize("lq,prefix,paged,bs", SPLIT_CASES)
+def test_prefill_split_long_rows(pkv, lq, prefix, paged, bs):
+    """Long rows cut into key-range pieces whose partial states a second kernel merges [P2 §5.2 ②]: every row
+    against the oracle, and within one bf16 rounding of the unplanned (unsplit) launch."""
+    lk = [a + b for a, b in zip(lq, prefix)]
+    case = workloads.make_case(lq, lk, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=bs,
+                               num_blocks=sum(math.ceil(c / bs) for c in lk) + 2, dtype="bf16", seed=sum(lk))
+    log(f"split pieces lq={lq} prefix={prefix} paged={paged} bs={bs}")
+    out, *_ = _run_step(pkv, case, paged=paged, order=True)
+    _check_attention(case, out)
+    ref, *_ = _run_step(pkv, case, paged=paged, order=False)
+    torch.testing.assert_close(out.float(), ref.float(), rtol=2.0 ** -7, atol=1e-3)
 
 
 def test_prefill_order_workspace(pkv):
