@@ -825,8 +825,8 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_split_plan_kernel(Prefil
   __shared__ int sc0[PLAN_MAX_BATCH], snk[PLAN_MAX_BATCH];
   __shared__ int start[PLAN_BUCKETS];       // bucket i holds pieces of `buckets` - i key tiles (clamped)
   __shared__ int chunk[PLAN_THREADS];
-  __shared__ unsigned long long s_w;
-  __shared__ int s_max, s_pieces, s_split, s_parts, s_sid, s_pbase;
+  __shared__ unsigned long long s_w[PLAN_THREADS / 64];
+  __shared__ int s_pieces, s_split, s_parts, s_sid, s_pbase;
   const int tid = threadIdx.x, nb = pa.batch, nbk = pa.buckets;
   for (int b = tid; b < nb; b += PLAN_THREADS) {
     const SeqGeom g = seq_geom(p, b);
@@ -835,10 +835,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_split_plan_kernel(Prefil
     snk[b] = g.NKe;
   }
   for (int i = tid; i < nbk; i += PLAN_THREADS) start[i] = 0;
-  if (tid == 0) {
-    s_w = 0;
-    s_max = s_pieces = s_split = s_parts = s_sid = s_pbase = 0;
-  }
+  if (tid == 0) s_pieces = s_split = s_parts = s_sid = s_pbase = 0;
   __syncthreads();
   const int units = min(block_exclusive_scan(uoff, nb, chunk), pa.unit_cap);
   if (tid == 0) uoff[nb] = units;
@@ -856,27 +853,33 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_split_plan_kernel(Prefil
   };
   {
     unsigned long long w = 0;
-    int mx = 0;
     for (int u = tid; u < units; u += PLAN_THREADS) {
       int b, t;
-      const int nk = locate(u, b, t);
-      w += unsigned(nk);
-      mx = max(mx, nk);
+      w += unsigned(locate(u, b, t));
     }
-    atomicAdd(&s_w, w);
-    atomicMax(&s_max, mx);
+    // the total over the work-group: wave sums by lane shuffles, then one value per wave
+    for (int off = 32; off >= 1; off >>= 1) {
+      const unsigned lo = __shfl_xor(unsigned(w), off), hi = __shfl_xor(unsigned(w >> 32), off);
+      w += (static_cast<unsigned long long>(hi) << 32) | lo;
+    }
+    if ((tid & 63) == 0) s_w[tid >> 6] = w;
   }
   __syncthreads();
-  const unsigned long long share = (s_w * unsigned(p.num_kv_heads) + unsigned(pa.slots) - 1) / unsigned(pa.slots);
+  unsigned long long wsum = 0;
+#pragma unroll
+  for (int i = 0; i < PLAN_THREADS / 64; ++i) wsum += s_w[i];
+  const unsigned long long share = (wsum * unsigned(p.num_kv_heads) + unsigned(pa.slots) - 1) / unsigned(pa.slots);
   const int P = int(min(max(share, (unsigned long long)kPieceMin), (unsigned long long)INT32_MAX));
-  auto npieces = [&](int nk) { return nk > P ? (nk + P - 1) / P : 1; };
+  auto npieces = [&](int nk) { return nk > P ? int((int64_t(nk) + P - 1) / P) : 1; };
+  // first key tile of piece k of np (k = np: the end); 64-bit products for the longest key ranges
+  auto cut_at = [](int k, int nk, int np) { return int(int64_t(k) * nk / np); };
   auto bucket = [&](int len) { return nbk - min(len, nbk); };
-  bool split = true;
+  bool listed = true;
   {  // counting pass
     for (int u = tid; u < units; u += PLAN_THREADS) {
       int b, t;
       const int nk = locate(u, b, t), np = npieces(nk);
-      for (int k = 0; k < np; ++k) atomicAdd(&start[bucket((k + 1) * nk / np - k * nk / np)], 1);
+      for (int k = 0; k < np; ++k) atomicAdd(&start[bucket(cut_at(k + 1, nk, np) - cut_at(k, nk, np))], 1);
       atomicAdd(&s_pieces, np);
       if (np > 1) {
         atomicAdd(&s_split, 1);
@@ -885,9 +888,9 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_split_plan_kernel(Prefil
     }
     __syncthreads();
     // The bounds above guarantee these fit; the check keeps an inconsistent sizing from writing past the lists.
-    split = s_pieces <= pa.list_cap && s_split <= pa.split_cap && s_parts <= 2 * pa.split_cap;
+    listed = s_pieces <= pa.list_cap && s_split <= pa.split_cap && s_parts <= 2 * pa.split_cap;
   }
-  if (!split) {
+  if (!listed) {
     if (tid == 0) {
       pa.hdr[0] = 0;
       pa.hdr[1] = 0;
@@ -906,7 +909,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) prefill_split_plan_kernel(Prefil
       pa.splits[sid] = PrefillSplit{b, t, np, pbase};
     }
     for (int k = 0; k < np; ++k) {
-      const int k0 = k * nk / np, k1 = (k + 1) * nk / np;
+      const int k0 = cut_at(k, nk, np), k1 = cut_at(k + 1, nk, np);
       const int pos = atomicAdd(&start[bucket(k1 - k0)], 1);
       pa.list[pos] = PrefillPiece{b, t, k0, k1, np > 1 ? pbase + k : -1, 0, 0, 0};
     }
