@@ -19,10 +19,12 @@ The same JSON line carries:
                 before the GPU is touched): decode attention of the whole batch-64 decode workload, with the
                 varlen prefill (TFLOP/s) and the store sweep (GB/s) beside it;
   secondary     the unfused decode step and call, varlen prefill TFLOP/s (8 sequences of 128-2048), prefix-cache
-                prefill TFLOP/s (16 sequences), the store sweep GB/s (N=16384), the long padded decode GB/s
-                (batch 256) and the fused QK-Norm + RoPE + store GB/s (the 8 prefill sequences' tokens); the
-                bandwidth-bound ones rotate enough independent inputs (``sets_rotated``) that each call reads
-                from HBM, not from rows the last-level cache kept from an earlier call.
+                prefill TFLOP/s (16 sequences), chunked prefill on 16k/32k-token cached prefixes (with and without
+                the splitting of long key ranges), the platform BLAS's bf16 GEMM rate (the practical matrix-core
+                rate under full load), the store sweep GB/s (N=16384), the long padded decode GB/s (batch 256)
+                and the fused QK-Norm + RoPE + store GB/s (the 8 prefill sequences' tokens); the bandwidth-bound
+                ones rotate enough independent inputs (``sets_rotated``) that each call reads from HBM, not from
+                rows the last-level cache kept from an earlier call.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu]
 """
@@ -180,6 +182,44 @@ def prefill_flops(case):
     return 4 * case.head_dim * case.num_q_heads * pairs
 
 
+CHUNKED_SHAPES = (("chunked_prefill_1x512_on_32k", [512], [32768]),
+                  ("chunked_prefill_4x256_on_16k", [256] * 4, [16384] * 4))
+
+
+def bench_chunked_prefill(pkv, torch, steps):
+    """New-token chunks on long cached prefixes (few query tiles over long key ranges): the call as the library
+    runs it (the planner cuts the long key ranges into pieces merged by a second kernel) and, for reference, the
+    same call without a workspace (each query tile walks its whole key range in one work-group)."""
+    import workloads
+    out = {}
+    for name, chunks, prefixes in CHUNKED_SHAPES:
+        c = workloads.chunked_prefill(chunks, prefixes, device="cuda")
+        kc, vc = build_caches(pkv, torch, c)
+        bt = torch.from_numpy(c.block_tables).cuda()
+        cu_q = torch.from_numpy(c.cu_seqlens_q).cuda()
+        cu_k = torch.from_numpy(c.cu_seqlens_k).cuda()
+        n = int(c.cu_seqlens_q[-1])
+        sm = pkv.kv_slot_mapping(bt, c.block_size, n, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+        pkv.kv_store(c.k, c.v, kc, vc, sm)
+        res = torch.empty_like(c.q)
+        mq, mk = int(c.Lq.max()), int(c.Lk.max())
+        ws = torch.empty(pkv.attn_prefill_workspace_bytes(c.batch, n, mq, 16, 8, 128), dtype=torch.uint8,
+                         device="cuda")
+        split_ms = time_kernel(torch, lambda i: pkv.attn_prefill_varlen(
+            c.q, kc, vc, cu_q, cu_k, mq, mk, c.scale, block_table=bt, out=res, workspace=ws), max(steps // 4, 10))
+        whole_ms = time_kernel(torch, lambda i: pkv.attn_prefill_varlen(
+            c.q, kc, vc, cu_q, cu_k, mq, mk, c.scale, block_table=bt, out=res, order=False), max(steps // 4, 10))
+        flops = prefill_flops(c)
+        out[name] = {"value": round(flops / (split_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                     "kernel_ms": round(split_ms, 4), "flops": flops,
+                     "without_split_TFLOPs": round(flops / (whole_ms * 1e-3) / 1e12, 2),
+                     "without_split_kernel_ms": round(whole_ms, 4),
+                     "shape": f"{len(chunks)} x {chunks[0]} new tokens on {prefixes[0]}-token cached prefixes"}
+        del kc, vc, ws, res, c
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_gemm_reference(torch, n=8192, reps=20):
     """The platform BLAS (hipBLASLt through torch.matmul) on an n^3 bf16 product: the dense matrix-core rate this GPU
     sustains under full load, where its clock is held well below the 2.4 GHz the 2.5 PFLOP/s figure assumes."""
@@ -274,12 +314,22 @@ def bench_store(pkv, torch, steps, warmup):
         dst_k.copy_(sw.key[s].view(-1, d))
         dst_v.copy_(sw.value[s].view(-1, d))
 
+    # The same kernel with each set's rows stored to consecutive slots (its own region of the cache): the same
+    # bytes and launch, the destination contiguous -- what placing 2 KiB rows at random slots costs.
+    seq = [torch.arange(s * n, (s + 1) * n, dtype=torch.int32, device="cuda") for s in range(len(slots))]
+
+    def store_sequential(i):
+        s = i % len(slots)
+        pkv.kv_store(sw.key[s], sw.value[s], kc, vc, seq[s])
+
     scatter_ms = time_kernel(torch, torch_scatter, steps)
     copy_ms = time_kernel(torch, torch_copy, steps)
+    seq_ms = time_kernel(torch, store_sequential, steps)
     del kc, vc, kflat, vflat, dst_k, dst_v
     torch.cuda.empty_cache()
     return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n, "sets": len(slots),
-            "torch_scatter_ms": scatter_ms, "torch_copy_ms": copy_ms, "copy_bytes": 2 * n * row * 2}
+            "torch_scatter_ms": scatter_ms, "torch_copy_ms": copy_ms, "copy_bytes": 2 * n * row * 2,
+            "sequential_slots_ms": seq_ms}
 
 
 LAYERS_PER_GRAPH = 8
@@ -567,8 +617,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--only", choices=["prefill", "prefix", "store", "long_decode", "qknorm_rope", "unfused_decode",
-                                       "decode_latency", "sublayer"],
+    ap.add_argument("--only", choices=["prefill", "prefix", "chunked", "store", "long_decode", "qknorm_rope",
+                                       "unfused_decode", "decode_latency", "sublayer"],
                     default=None,
                     help="run just one secondary workload (after the headline), e.g. for a profiler")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -605,7 +655,7 @@ def main():
     secondary = {}
     if not args.headline_only:
         want = lambda name: args.only in (None, name)
-        p3 = p4 = st = d5 = qr = fd = dl = sb = None
+        p3 = p4 = st = d5 = qr = fd = dl = sb = ch = None
         if want("unfused_decode"):
             log("unfused decode step (slot_mapping, store, decode), batch 64")
             fd = bench_decode(pkv, torch, workloads.decode_batch64, args.steps, args.warmup, args.layers)
@@ -615,6 +665,9 @@ def main():
         if want("prefix"):
             log("prefix prefill, 16 sequences")
             p4 = bench_prefill(pkv, torch, workloads.prefix_prefill_16seq, args.steps, args.warmup, args.layers, paged=True)
+        if want("chunked"):
+            log("chunked prefill on long cached prefixes")
+            ch = bench_chunked_prefill(pkv, torch, args.steps)
         if want("store"):
             log("store sweep, 16384 tokens")
             st = bench_store(pkv, torch, args.steps, args.warmup)
@@ -658,7 +711,9 @@ def main():
                                                  "reference_torch_index_copy_GBps":
                                                      round(st["copy_bytes"] / (st["torch_scatter_ms"] * 1e-3) / 1e9, 1),
                                                  "reference_contiguous_copy_GBps":
-                                                     round(st["copy_bytes"] / (st["torch_copy_ms"] * 1e-3) / 1e9, 1)}
+                                                     round(st["copy_bytes"] / (st["torch_copy_ms"] * 1e-3) / 1e9, 1),
+                                                 "same_kernel_sequential_slots_GBps":
+                                                     round(st["bytes"] / (st["sequential_slots_ms"] * 1e-3) / 1e9, 1)}
         if fd is not None:
             gbk = fd["kv_bytes"] / (fd["kernel_ms"] * 1e-3) / 1e9
             secondary["decode_step_unfused_batch64"] = {
@@ -672,6 +727,8 @@ def main():
                                                        "frac_hbm_peak": round(gbq / HBM_PEAK_GBS, 4),
                                                        "kernel_ms": round(qr["kernel_ms"], 5), "bytes": qr["bytes"],
                                                        "tokens": qr["tokens"], "sets_rotated": max(args.layers, 8)}
+        if ch is not None:
+            secondary.update(ch)
         if dl is not None:
             secondary["decode_step_latency_padded_batches"] = dl
         if sb is not None:

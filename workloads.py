@@ -224,6 +224,17 @@ def prefix_prefill_16seq(device="cpu", seed=4):
                      num_blocks=4096, dtype="bf16", seed=seed, device=device, max_blocks=18, rng=rng)
 
 
+def chunked_prefill(chunks, prefixes, device="cpu", seed=6):
+    """New-token chunks on long cached prefixes (chunked prefill: few query tiles over long key ranges), paged
+    bf16 16/8/128 cache with block_size 256; the history is each sequence's cached prefix."""
+    rng = np.random.default_rng(seed)
+    chunks, prefixes = np.asarray(chunks, np.int64), np.asarray(prefixes, np.int64)
+    lk = chunks + prefixes
+    num_blocks = int(sum(-(-x // 256) for x in lk)) + 16
+    return make_case(chunks, lk, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+                     num_blocks=num_blocks, dtype="bf16", seed=seed, device=device, rng=rng)
+
+
 def long_decode_batch256(device="cpu", seed=5):
     """224 real rows followed by 32 padding rows (context 0, slot -1, block row all -1)."""
     rng = np.random.default_rng(seed)
