@@ -68,8 +68,10 @@ def test_decode_step_graph_replays(pkv):
         del scratch
 
 
-def test_prefix_prefill_graph_replays(pkv):
-    lq, prefix = [200, 64, 1], [1000, 0, 3000]
+@pytest.mark.parametrize("lq,prefix", [([200, 64, 1], [1000, 0, 3000]), ([64], [20000])])
+def test_prefix_prefill_graph_replays(pkv, lq, prefix):
+    """A prefix-cache prefill with the planner's workspace, captured once and replayed: both cases have too few
+    query tiles to fill the GPU, so the captured launches are the planner, the key-range pieces and their merge."""
     lk = [a + b for a, b in zip(lq, prefix)]
     case = workloads.make_case(lq, lk, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
                                num_blocks=sum(math.ceil(c / 256) for c in lk) + 2, dtype="bf16", seed=92)
@@ -78,11 +80,12 @@ def test_prefix_prefill_graph_replays(pkv):
     pkv.kv_store(to_dev(case.k, "bf16"), to_dev(case.v, "bf16"), kc, vc, gpu_slot_mapping(case))
     q = to_dev(case.q, "bf16")
     cu_q, cu_k, bt = i32(case.cu_seqlens_q), i32(case.cu_seqlens_k), i32(case.block_tables)
-    ws = torch.empty(pkv.attn_prefill_workspace_bytes(3, sum(lq), 200, 16, 8, 128), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(pkv.attn_prefill_workspace_bytes(len(lq), sum(lq), max(lq), 16, 8, 128), dtype=torch.uint8,
+                     device="cuda")
     out = torch.empty_like(q)
 
     def call():
-        pkv.attn_prefill_varlen(q, kc, vc, cu_q, cu_k, 200, max(lk), case.scale, block_table=bt, out=out,
+        pkv.attn_prefill_varlen(q, kc, vc, cu_q, cu_k, max(lq), max(lk), case.scale, block_table=bt, out=out,
                                 workspace=ws)
 
     call()
