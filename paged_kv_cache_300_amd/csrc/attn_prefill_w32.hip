@@ -314,10 +314,11 @@ __global__ void __launch_bounds__(256, kW32PerCU) prefill_w32_kernel(PrefillKern
 }
 
 // Merge of the split units: one work-group per (split unit, kv head, 32-dim block db of the output), the lanes laid
-// out as the main kernel's, so each lane combines its own (m, l) and O block of every piece: with M the largest m,
-// O = sum O_i 2^(m_i - M) and l = sum l_i 2^(m_i - M) -- the exact online-softmax rescaling [P2 §5.2 ②] (a piece
-// in which a row saw no key has m = -1e30 and contributes nothing).  The loads of several pieces are in flight at
-// once (the loops are unrolled), so a unit cut into many pieces does not pay one memory round trip per piece.
+// out as the main kernel's, so each lane combines its own (m, l) and O block of every piece by the exact online-
+// softmax rescaling [P2 §5.2 ②]: with M the running maximum, a new piece (m_i, l_i, O_i) gives M' = max(M, m_i),
+// l = l 2^(M - M') + l_i 2^(m_i - M'), O likewise (a piece in which a row saw no key has m = -1e30, l = 0, O = 0
+// and changes nothing).  One pass, unrolled so that the loads of eight pieces are in flight at once: a unit cut
+// into many pieces pays a memory round trip per eight pieces, not per piece.
 __global__ void __launch_bounds__(256) prefill_w32_merge_kernel(PrefillKernelArgs p, PieceList plan) {
   const int db = int(blockIdx.x & 3u);
   const int kvh = int((blockIdx.x >> 2) % unsigned(p.num_kv_heads));
@@ -330,29 +331,39 @@ __global__ void __launch_bounds__(256) prefill_w32_merge_kernel(PrefillKernelArg
   const int tok = e.t * BM + 32 * (wave >> 1) + j;
   const f32x4_t* src = plan.parts + ((size_t(e.pbase) * p.num_kv_heads + kvh) * 4 + wave) * (kPartialChunks * 64) + lane;
   const size_t piece_stride = size_t(p.num_kv_heads) * 4 * kPartialChunks * 64;
-  float mmax = kMinusBig;
-#pragma unroll 8
-  for (int i = 0; i < e.np; ++i) mmax = fmaxf(mmax, src[i * piece_stride + 16 * 64][0]);
-  f32x16_t o[1];
+  float mrun = kMinusBig, l = 0.f;
+  f32x16_t o;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) o[0][r] = 0.f;
-  float l = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < e.np; ++i) {
-    const f32x4_t* q = src + i * piece_stride;
-    const f32x4_t ml = q[16 * 64];
-    f32x4_t x[4];
+  for (int r = 0; r < 16; ++r) o[r] = 0.f;
+  constexpr int kBatch = 8;
+  for (int i0 = 0; i0 < e.np; i0 += kBatch) {
+    // all loads of the batch first (pieces past the last re-read it and are then left out)
+    f32x4_t ml[kBatch], x[kBatch][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) x[v] = q[(4 * db + v) * 64];
-    const float f = fast_exp2(ml[0] - mmax);
-    l = fmaf(ml[1], f, l);
+    for (int k = 0; k < kBatch; ++k) {
+      const f32x4_t* q = src + size_t(min(i0 + k, e.np - 1)) * piece_stride;
+      ml[k] = q[16 * 64];
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < 4; ++v) x[k][v] = q[(4 * db + v) * 64];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keeps the batch's loads ahead of the arithmetic that waits for them
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[0][4 * v + k] = fmaf(x[v][k], f, o[0][4 * v + k]);
+    for (int k = 0; k < kBatch; ++k) {
+      // a re-read entry past the last piece folds in with weight 0 and leaves the running maximum alone
+      const bool ok = i0 + k < e.np;
+      const float mi = ok ? ml[k][0] : kMinusBig;
+      const float mn = fmaxf(mrun, mi);
+      const float a = fast_exp2(mrun - mn), f = ok ? fast_exp2(mi - mn) : 0.f;
+      mrun = mn;
+      l = fmaf(ml[k][1], f, l * a);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[4 * v + c] = fmaf(x[k][v][c], f, o[4 * v + c] * a);
+    }
   }
   if (tok >= Lq || int64_t(q_start) + tok >= p.num_q_tokens) return;
-  write_block(p, int64_t(q_start) + tok, kvh * 2 + (wave & 1), half, db, o[0], row_inverse(l));
+  write_block(p, int64_t(q_start) + tok, kvh * 2 + (wave & 1), half, db, o, row_inverse(l));
 }
 
 }  // namespace
