@@ -124,9 +124,11 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 }
 
 // Workers that get keys: at most the launched W, and at least MIN_KEYS keys each, so that a small batch is not
-// cut into hundreds of tiny ranges whose partial outputs cost more to merge than to compute (batch 1 with 2.9k
-// keys: 60 -> 23 us per step).  Every work-group and the combine kernel derive it from T the same way.
-constexpr int MIN_KEYS = 128;
+// cut into hundreds of tiny ranges whose partial outputs cost more to merge than to compute (one row of 2.9k keys
+// over every worker: 60 us per step).  Measured on MI355X per decode step at 1 / 8 rows (2.9k / 13k keys): 20.3 /
+// 26.8 us with at least 128 keys per worker, 19.3 / 25.1 with 64, 23.3 / 29.5 with 32; batch 64 and up have more
+// keys than that per worker.  Every work-group and the combine kernel derive it from T the same way.
+constexpr int MIN_KEYS = 64;
 __device__ __forceinline__ int active_workers(int64_t T, int W) {
   return int(max(int64_t(1), min(int64_t(W), T / MIN_KEYS)));
 }
