@@ -9,8 +9,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import (BF16_TOL, F32_TOL, f64, gpu_slot_mapping, gpu_store_history, host_of, i32, log, max_abs_err,
-                      nan_cache, oracle_attention, oracle_slot_mapping, to_dev, to_host)
+from gpu_util import (BF16_TOL, F32_TOL, f64, gpu_slot_mapping, gpu_store_history, host_of, i32, log, logical_kv,
+                      max_abs_err, nan_cache, oracle_attention, oracle_slot_mapping, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -245,6 +245,49 @@ def test_prefill_split_long_rows(pkv, lq, prefix, paged, bs):
     _check_attention(case, out)
     ref, *_ = _run_step(pkv, case, paged=paged, order=False)
     torch.testing.assert_close(out.float(), ref.float(), rtol=2.0 ** -7, atol=1e-3)
+
+
+SPLIT_HEAD_CASES = [
+    # (lq, prefix, paged, block_size, hq, hkv): the same cut at other head counts (GQA groups of 2), so the
+    # workspace's per-kv-head partial slots and the merge's (unit, kv head) grid are exercised beyond 8 kv heads:
+    # 19 query tiles x 16 kv heads of one 1200-token sequence, and chunks on long prefixes with 4 kv heads
+    ([1200], [0], False, 256, 32, 16),
+    ([64, 128], [9000, 3000], True, 128, 8, 4),
+]
+
+
+@pytest.mark.parametrize("lq,prefix,paged,bs,hq,hkv", SPLIT_HEAD_CASES)
+def test_prefill_split_other_head_counts(pkv, lq, prefix, paged, bs, hq, hkv):
+    lk = [a + b for a, b in zip(lq, prefix)]
+    case = workloads.make_case(lq, lk, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=bs,
+                               num_blocks=sum(math.ceil(c / bs) for c in lk) + 2, dtype="bf16", seed=7 + sum(lk))
+    log(f"split pieces lq={lq} prefix={prefix} paged={paged} bs={bs} heads {hq}/{hkv}")
+    out, *_ = _run_step(pkv, case, paged=paged, order=True)
+    _check_attention(case, out)
+    ref, *_ = _run_step(pkv, case, paged=paged, order=False)
+    torch.testing.assert_close(out.float(), ref.float(), rtol=2.0 ** -7, atol=1e-3)
+
+
+def test_prefill_one_long_sequence_sampled_rows(pkv):
+    """One 6000-token causal sequence from contiguous rows: 94 query tiles, the last over 94 key tiles (the 32x32
+    kernel in grid order).  Sampled rows against the oracle, row i as its own problem: one query at position i over
+    keys 0..i [P2 §5.3, causal varlen call], which is what the causal mask leaves of the whole sequence."""
+    L = 6000
+    case = workloads.make_case([L], [L], num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+                               num_blocks=math.ceil(L / 256) + 2, dtype="bf16", seed=6000)
+    out, *_ = _run_step(pkv, case, paged=False, order=True)
+    got = oracle.as_f64(to_host(out), "bf16")
+    q = f64(case.q, "bf16")
+    k = oracle.as_f64(logical_kv(case, 0, "k"), "bf16")
+    v = oracle.as_f64(logical_kv(case, 0, "v"), "bf16")
+    rng = np.random.default_rng(6000)
+    rows = sorted(set(rng.integers(0, L, 48).tolist()) | {0, 1, 63, 64, 4095, 4096, L - 65, L - 1})
+    worst = 0.0
+    for i in rows:
+        want = oracle.attention_ref(q[i:i + 1], k[:i + 1], v[:i + 1], [0, 1], [0, i + 1], case.scale, causal=True)
+        worst = max(worst, max_abs_err(got[i:i + 1], want))
+    log(f"  {len(rows)} sampled rows, max-abs error {worst:.3e} (tol {BF16_TOL:.0e})")
+    assert worst <= BF16_TOL
 
 
 def test_prefill_order_workspace(pkv):
