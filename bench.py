@@ -14,7 +14,9 @@ The same JSON line carries:
                 on around K back-to-back calls over the same rotated caches (an event record per call would
                 make the GPU drain before each one), against MI355X's 8 TB/s HBM peak; ``traffic`` from
                 rocprofv3 counters kept in profiles/ (null if the kernel source changed since they were
-                taken);
+                taken); ``kernel_ms_spread`` gives the median and the minimum ms per call over chunks of 50
+                calls of a second pass (events at chunk boundaries only), as the decode, prefill and store
+                entries do;
   cpu_baseline  the CPU oracle on the host's cores (a pool of worker processes, one BLAS thread each, run
                 before the GPU is touched): decode attention of the whole batch-64 decode workload, with the
                 varlen prefill (TFLOP/s) and the store sweep (GB/s) beside it;
@@ -99,6 +101,26 @@ def time_kernel(torch, call, n):
     return start.elapsed_time(end) / n
 
 
+def time_kernel_spread(torch, call, n, per_chunk=50):
+    """The same back-to-back calls as time_kernel, in chunks of ``per_chunk`` with an event at each chunk boundary
+    only: the median and the minimum over chunks of the ms per call (a separate pass, so the events between chunks
+    do not touch the mean the line reports)."""
+    chunks = max(1, n // per_chunk)
+    for i in range(2):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(chunks + 1)]
+    ev[0].record()
+    for c in range(chunks):
+        for i in range(per_chunk):
+            call(c * per_chunk + i)
+        ev[c + 1].record()
+    torch.cuda.synchronize()
+    per_call = sorted(ev[c].elapsed_time(ev[c + 1]) / per_chunk for c in range(chunks))
+    return {"median_ms": round(per_call[len(per_call) // 2], 5), "min_ms": round(per_call[0], 5),
+            "chunks": chunks, "calls_per_chunk": per_chunk}
+
+
 def dev_case_layers(make, layers, torch):
     """``layers`` independent draws of one workload's tensors (same metadata, different data and caches)."""
     import workloads
@@ -168,10 +190,11 @@ def bench_decode(pkv, torch, make, steps, warmup, layers, fused=False):
 
     wall_ms = run_steps(torch, step, steps, warmup)
     kern_ms = time_kernel(torch, lambda i: (fused_step if fused else attend)(i % layers), steps)
+    spread = time_kernel_spread(torch, lambda i: (fused_step if fused else attend)(i % layers), steps)
     kv_bytes = int(c0.Lk.astype(int).sum()) * 2 * c0.num_kv_heads * c0.head_dim * 2
     del caches, cases
     torch.cuda.empty_cache()
-    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "kv_bytes": kv_bytes, "batch": c0.batch,
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "spread": spread, "kv_bytes": kv_bytes, "batch": c0.batch,
             "sum_ctx": int(c0.Lk.astype(int).sum())}
 
 
@@ -269,10 +292,11 @@ def bench_prefill(pkv, torch, make, steps, warmup, layers, paged):
 
     wall_ms = run_steps(torch, step, steps, warmup)
     kern_ms = time_kernel(torch, lambda i: attn(cases[i % layers], *caches[i % layers], i % layers), steps)
+    spread = time_kernel_spread(torch, lambda i: attn(cases[i % layers], *caches[i % layers], i % layers), steps)
     flops = prefill_flops(c0)
     del caches, cases
     torch.cuda.empty_cache()
-    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "flops": flops, "tokens": n}
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "spread": spread, "flops": flops, "tokens": n}
 
 
 def bench_store(pkv, torch, steps, warmup):
@@ -290,6 +314,7 @@ def bench_store(pkv, torch, steps, warmup):
 
     wall_ms = run_steps(torch, step, steps, warmup)
     kern_ms = time_kernel(torch, step, steps)
+    spread = time_kernel_spread(torch, step, steps)
     n = len(sw.slots[0])
     row = sw.num_kv_heads * sw.head_dim * 2
     moved = 2 * n * row * 2 + 4 * n  # read + write of K and V rows, plus the slots
@@ -327,7 +352,7 @@ def bench_store(pkv, torch, steps, warmup):
     seq_ms = time_kernel(torch, store_sequential, steps)
     del kc, vc, kflat, vflat, dst_k, dst_v
     torch.cuda.empty_cache()
-    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "bytes": moved, "tokens": n, "sets": len(slots),
+    return {"wall_ms": wall_ms, "kernel_ms": kern_ms, "spread": spread, "bytes": moved, "tokens": n, "sets": len(slots),
             "torch_scatter_ms": scatter_ms, "torch_copy_ms": copy_ms, "copy_bytes": 2 * n * row * 2,
             "sequential_slots_ms": seq_ms}
 
@@ -649,8 +674,8 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic("attn_decode_paged_store_decode_batch64", dec_hash),
                 "kernel": "attn_decode_paged_store (decode_lean_kernel<2, store> + decode_combine_kernel)",
-                "kernel_ms": round(dec["kernel_ms"], 5), "algorithmic_bytes": dec["kv_bytes"],
-                "source_hash": dec_hash}
+                "kernel_ms": round(dec["kernel_ms"], 5), "kernel_ms_spread": dec["spread"],
+                "algorithmic_bytes": dec["kv_bytes"], "source_hash": dec_hash}
 
     secondary = {}
     if not args.headline_only:
@@ -700,13 +725,14 @@ def main():
             secondary[name] = {"value": round(tf, 2), "unit": "TFLOP/s", "frac_bf16_mfma_peak":
                                round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                                "frac_of_bf16_gemm_reference": round(tf / gemm, 4),
-                               "kernel_ms": round(r["kernel_ms"], 4),
+                               "kernel_ms": round(r["kernel_ms"], 4), "kernel_ms_spread": r["spread"],
                                "step_ms": round(r["wall_ms"], 4), "flops": r["flops"], "tokens": r["tokens"]}
         if st is not None:
             gbs = st["bytes"] / (st["kernel_ms"] * 1e-3) / 1e9
             secondary["store_sweep_16k"] = {"value": round(gbs, 1), "unit": "GB/s",
                                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                                 "kernel_ms": round(st["kernel_ms"], 5), "bytes": st["bytes"],
+                                                 "kernel_ms": round(st["kernel_ms"], 5),
+                                                 "kernel_ms_spread": st["spread"], "bytes": st["bytes"],
                                                  "tokens": st["tokens"], "sets_rotated": st["sets"],
                                                  "reference_torch_index_copy_GBps":
                                                      round(st["copy_bytes"] / (st["torch_scatter_ms"] * 1e-3) / 1e9, 1),
