@@ -420,6 +420,30 @@ def bench_decode_latency(pkv, torch, reps):
     return res
 
 
+def bench_prefill_data(pkv, torch, steps):
+    """The same prefill call on the same shapes with different K/V values: N(0,1) (as every workload), all zero,
+    all 1.0, then N(0,1) again.  The kernels run the same instructions either way; a rate that moves with the
+    values shows the chip's power limit (operands that switch fewer bits draw less power, so the clock stays
+    higher), not the instruction stream, setting the pace.  Dense rows: 32 sequences of 2048 tokens, non-causal,
+    contiguous K/V."""
+    B, L = 32, 2048
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2048)
+    q = torch.randn(B * L, 16, 128, device="cuda", generator=gen).to(torch.bfloat16)
+    k = torch.randn(B * L, 8, 128, device="cuda", generator=gen).to(torch.bfloat16)
+    v = torch.randn(B * L, 8, 128, device="cuda", generator=gen).to(torch.bfloat16)
+    cu = torch.arange(0, (B + 1) * L, L, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    flops = 4 * 128 * 16 * B * L * L
+    res = {"shape": "32 x 2048 tokens, non-causal, bf16 16/8/128, contiguous K/V", "flops": flops}
+    for name, kk, vv in (("randn", k, v), ("zero", torch.zeros_like(k), torch.zeros_like(v)),
+                         ("ones", torch.ones_like(k), torch.ones_like(v)), ("randn_again", k, v)):
+        ms = time_kernel(torch, lambda i: pkv.attn_prefill_varlen(q, kk, vv, cu, cu, L, L, 128 ** -0.5,
+                                                                  causal=False, out=out), max(steps // 10, 20))
+        res[f"kv_{name}_TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    return res
+
+
 def bench_sublayer(pkv, torch, steps, warmup):
     """The synthetic-weight attention sub-layer (qkv GEMM, QK-Norm + RoPE + store, paged attention, o GEMM):
     a prefill step over the 8 varlen prefill sequences and a decode step over the batch-64 decode workload."""
@@ -643,7 +667,7 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="independent caches rotated over the steps")
     ap.add_argument("--headline-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--only", choices=["prefill", "prefix", "chunked", "store", "long_decode", "qknorm_rope",
-                                       "unfused_decode", "decode_latency", "sublayer"],
+                                       "unfused_decode", "decode_latency", "sublayer", "prefill_data"],
                     default=None,
                     help="run just one secondary workload (after the headline), e.g. for a profiler")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -680,7 +704,7 @@ def main():
     secondary = {}
     if not args.headline_only:
         want = lambda name: args.only in (None, name)
-        p3 = p4 = st = d5 = qr = fd = dl = sb = ch = None
+        p3 = p4 = st = d5 = qr = fd = dl = sb = ch = pdv = None
         if want("unfused_decode"):
             log("unfused decode step (slot_mapping, store, decode), batch 64")
             fd = bench_decode(pkv, torch, workloads.decode_batch64, args.steps, args.warmup, args.layers)
@@ -707,6 +731,9 @@ def main():
         if want("sublayer"):
             log("synthetic-weight attention sub-layer, workloads 3 (prefill) and 2 (decode)")
             sb = bench_sublayer(pkv, torch, args.steps, args.warmup)
+        if args.only == "prefill_data":  # on request only: it does not measure a workload
+            log("prefill rate against the K/V values (same shapes and instructions)")
+            pdv = bench_prefill_data(pkv, torch, args.steps)
         if want("long_decode"):
             log("long padded decode, batch 256")
             d5 = bench_decode(pkv, torch, workloads.long_decode_batch256, max(args.steps // 5, 3), 2, 2)
@@ -759,6 +786,8 @@ def main():
             secondary["decode_step_latency_padded_batches"] = dl
         if sb is not None:
             secondary["attention_sublayer"] = sb
+        if pdv is not None:
+            secondary["prefill_rate_vs_kv_values"] = pdv
         if d5 is not None:
             gbs5 = d5["kv_bytes"] / (d5["kernel_ms"] * 1e-3) / 1e9
             secondary["long_decode_batch256"] = {"value": round(gbs5, 1), "unit": "GB/s",
